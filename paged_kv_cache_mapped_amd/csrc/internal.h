@@ -1,0 +1,57 @@
+// Host-side launchers of the gfx950 kernels (called by capi.cpp after the
+// arguments have been validated).  Each returns hipSuccess or the launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+// ----------------------------------------------------------------- kv_write
+hipError_t launch_kv_write(const kv_cache_t& c, const void* k, const void* v,
+                           const int64_t* slots, int32_t num_tokens, hipStream_t s);
+
+// ----------------------------------------------------------------- pack
+hipError_t launch_pack(const kv_cache_t& c, const int32_t* ids, int32_t n, void* dst,
+                       bool unpack, hipStream_t s);
+
+// ----------------------------------------------------------------- decode
+struct DecodePlan {
+  int32_t split_tokens;   // tokens per split, multiple of 128
+  int32_t n_splits;       // splits of the longest request
+  int32_t n_gchunks;      // ceil(G / 16) groups of query heads per KV head
+};
+DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
+                       int32_t max_seq_len, int32_t split_tokens);
+size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_heads,
+                              int32_t head_dim);
+hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
+                         int32_t batch, int32_t num_q_heads, const int32_t* tables,
+                         int32_t max_blocks, const int32_t* seq_lens, float scale,
+                         void* out, float* lse, void* workspace, hipStream_t s);
+
+// ----------------------------------------------------------------- prefill / extend
+hipError_t launch_prefill(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
+                          int32_t num_q_heads, int32_t num_kv_heads, float scale,
+                          int32_t causal, void* out, float* lse, hipStream_t s);
+
+struct ExtendPlan {
+  int32_t chunk_tokens;   // cached tokens per chunk (multiple of block_size)
+  int32_t n_chunks;       // context chunks of the longest context
+  int32_t n_parts;        // n_chunks + 1 (the new-token part)
+};
+ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t max_ctx_len,
+                       int32_t chunk_budget_tokens);
+size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
+                              int32_t head_dim);
+hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,
+                         const void* k_new, const void* v_new, const int32_t* cu_q_lens,
+                         const int32_t* ctx_lens, const int32_t* tables, int32_t max_blocks,
+                         int32_t num_seqs, int32_t total_new, int32_t max_q_len,
+                         int32_t num_q_heads, float scale, void* out, float* lse,
+                         void* workspace, hipStream_t s);
+
+}  // namespace pkv

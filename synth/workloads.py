@@ -233,12 +233,15 @@ class DecodeStep:
 
 def decode_workload(seed, batch, num_q_heads, num_kv_heads, head_dim, block_size,
                     num_blocks, len_lo, len_hi, layout="nhd", dtype="bf16",
-                    growth: int = 0, max_blocks: Optional[int] = None) -> DecodeStep:
+                    growth: int = 0, max_blocks: Optional[int] = None,
+                    fixed_lens=None) -> DecodeStep:
     """``growth`` reserves table room for that many further tokens per request
-    (multi-step decode)."""
+    (multi-step decode); ``fixed_lens`` overrides the first lengths drawn."""
     rng = np.random.default_rng(seed)
     spec = CacheSpec(num_blocks, block_size, num_kv_heads, head_dim, layout, dtype)
     lens = rng.integers(len_lo, len_hi + 1, size=batch).astype(np.int32)
+    if fixed_lens is not None:
+        lens[:len(fixed_lens)] = fixed_lens
     tables = block_tables_for(rng, lens + growth, block_size, num_blocks, max_blocks)
     cache = random_cache(rng, spec)
     q = normal_bf16(rng, (batch, num_q_heads, head_dim))

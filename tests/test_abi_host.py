@@ -1,0 +1,173 @@
+"""Host-side tests of the C ABI (CPU only): the library loads without a GPU,
+exports every function include/pagedkv.h declares, rejects bad arguments with
+the documented status codes before any HIP call, and its host-only pieces
+(reorder, size queries) agree with the oracle and closed forms."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_mapped_amd as pk
+from oracle import batch as obatch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced by host validation
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    L = pk.lib()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pk.EXPORTS)
+    assert L.kv_abi_version() == 1
+
+
+def _cache(**kw):
+    c = dict(k_cache=FAKE, v_cache=FAKE, num_blocks=64, block_size=16, num_kv_heads=2,
+             head_dim=128, dtype=pk.KV_DTYPE_BF16, layout=pk.KV_LAYOUT_NHD, x=0,
+             k_scale=1.0, v_scale=1.0)
+    c.update(kw)
+    return pk.KVCacheT(**c)
+
+
+def _err():
+    return pk.lib().kv_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, pk.KV_ENOTSUP),
+    ("head_dim", 0, pk.KV_EINVAL),
+    ("block_size", 12, pk.KV_EINVAL),
+    ("block_size", 512, pk.KV_EINVAL),
+    ("num_blocks", 0, pk.KV_EINVAL),
+    ("num_kv_heads", 0, pk.KV_EINVAL),
+    ("dtype", 7, pk.KV_EINVAL),
+    ("layout", 3, pk.KV_EINVAL),
+    ("k_cache", 0, pk.KV_EINVAL),
+    ("k_cache", FAKE + 8, pk.KV_EINVAL),
+    ("k_scale", 2.0, pk.KV_EINVAL),
+])
+def test_cache_validation(field, value, code):
+    c = _cache(**{field: value})
+    rc = pk.lib().kv_write(ctypes.byref(c), FAKE, FAKE, FAKE, 4, None)
+    assert rc == code, _err()
+    assert _err() != "no error"
+
+
+def test_preshuffled_x_rules():
+    L = pk.lib()
+    c = _cache(layout=pk.KV_LAYOUT_PRESHUFFLED, x=16)          # bf16 needs x = 8
+    assert L.kv_write(ctypes.byref(c), FAKE, FAKE, FAKE, 1, None) == pk.KV_EINVAL
+    c = _cache(layout=pk.KV_LAYOUT_PRESHUFFLED, dtype=pk.KV_DTYPE_FP8_E4M3, x=16, block_size=8,
+               k_scale=0.5, v_scale=0.5)                        # bs must be a multiple of x
+    assert L.kv_write(ctypes.byref(c), FAKE, FAKE, FAKE, 1, None) == pk.KV_EINVAL
+    c = _cache(dtype=pk.KV_DTYPE_FP8_E4M3, k_scale=0.0, v_scale=1.0)
+    assert L.kv_write(ctypes.byref(c), FAKE, FAKE, FAKE, 1, None) == pk.KV_EINVAL
+
+
+def test_kv_write_argument_errors():
+    L = pk.lib()
+    c = _cache()
+    assert L.kv_write(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == pk.KV_EINVAL
+    assert L.kv_write(ctypes.byref(c), None, FAKE, FAKE, 4, None) == pk.KV_EINVAL
+    assert L.kv_write(ctypes.byref(c), FAKE + 2, FAKE, FAKE, 4, None) == pk.KV_EINVAL
+    assert L.kv_write(None, FAKE, FAKE, FAKE, 4, None) == pk.KV_EINVAL
+    # zero tokens: valid no-op, no HIP call
+    assert L.kv_write(ctypes.byref(c), None, None, None, 0, None) == pk.KV_OK
+
+
+def test_decode_argument_errors():
+    L = pk.lib()
+    c = _cache()
+    args = lambda **kw: dict(dict(q=FAKE, batch=4, hq=8, tables=FAKE, mb=32, lens=FAKE, msl=512,
+                                  scale=0.1, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30, split=0), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.paged_decode_ex(ctypes.byref(c), a["q"], a["batch"], a["hq"], a["tables"], a["mb"],
+                                 a["lens"], a["msl"], a["scale"], a["out"], a["lse"], a["ws"],
+                                 a["wsb"], a["split"], None)
+    assert call(hq=7) == pk.KV_EINVAL                 # not a multiple of H_kv
+    assert call(batch=0) == pk.KV_EINVAL
+    assert call(msl=0) == pk.KV_EINVAL
+    assert call(mb=8) == pk.KV_EINVAL                 # 8 blocks * 16 < 512 tokens
+    assert call(q=None) == pk.KV_EINVAL
+    assert call(out=FAKE + 4) == pk.KV_EINVAL
+    assert call(split=100) == pk.KV_EINVAL            # not a multiple of 128
+    assert call(split=128, wsb=16) == pk.KV_ENOSPC    # 4 splits need a workspace
+    assert call(split=128, ws=None) == pk.KV_EINVAL
+
+
+def test_decode_workspace_closed_form():
+    c = _cache(num_kv_heads=8)
+    L = pk.lib()
+    B, Hq, msl = 64, 64, 8192
+    for split in (128, 512, 1024):
+        n_splits = -(-msl // split)
+        rows = B * Hq * n_splits
+        want = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+        assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, Hq, msl, split) == want
+    assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, 63, msl, 0) == 0   # invalid -> 0
+
+
+def test_pack_sizes_and_errors():
+    L = pk.lib()
+    # Llama-3.1-70B layer: 8 KV heads x 128 dims x bf16 x 16 tokens -> 32 KiB per block per tensor
+    c = _cache(num_kv_heads=8, num_blocks=32768)
+    assert L.kv_layer_packed_bytes(ctypes.byref(c), 5000) == 327_680_000
+    assert L.kv_layer_packed_bytes(ctypes.byref(c), 1) * 80 // 16 == 320 * 1024
+    f = _cache(num_kv_heads=4, dtype=pk.KV_DTYPE_FP8_E4M3, layout=pk.KV_LAYOUT_PRESHUFFLED, x=16,
+               k_scale=0.1, v_scale=0.1)
+    assert L.kv_layer_packed_bytes(ctypes.byref(f), 3) == 2 * 3 * 16 * 4 * 128
+    assert L.kv_pack_layer(ctypes.byref(c), FAKE, 10, FAKE, 100, None) == pk.KV_ENOSPC
+    assert L.kv_unpack_layer(ctypes.byref(c), FAKE, 10, FAKE + 1, 1 << 30, None) == pk.KV_EINVAL
+    assert L.kv_pack_layer(ctypes.byref(c), FAKE, -1, FAKE, 1 << 30, None) == pk.KV_EINVAL
+    assert L.kv_pack_layer(ctypes.byref(c), None, 0, None, 0, None) == pk.KV_OK
+
+
+def test_prefill_and_extend_argument_errors():
+    L = pk.lib()
+    assert L.prefill_attn(FAKE, FAKE, FAKE, FAKE, 2, 100, 8, 3, 128, 0.1, 1, FAKE, None, None) == pk.KV_EINVAL
+    assert L.prefill_attn(FAKE, FAKE, FAKE, FAKE, 2, 100, 8, 2, 64, 0.1, 1, FAKE, None, None) == pk.KV_ENOTSUP
+    assert L.prefill_attn(FAKE, FAKE, FAKE, FAKE, 2, 100, 8, 2, 128, 0.1, 2, FAKE, None, None) == pk.KV_EINVAL
+    assert L.prefill_attn(None, FAKE, FAKE, FAKE, 2, 100, 8, 2, 128, 0.1, 1, FAKE, None, None) == pk.KV_EINVAL
+    assert L.prefill_attn(None, None, None, None, 0, 0, 8, 2, 128, 0.1, 1, None, None, None) == pk.KV_OK
+    c = _cache()
+    f = _cache(dtype=pk.KV_DTYPE_FP8_E4M3, k_scale=0.1, v_scale=0.1)
+    ext = lambda cc, budget=32768, mctx=100, mb=16: L.extend_attn(
+        ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mb, 2, 64, 32, mctx, 8, budget, 0.1,
+        FAKE, None, FAKE, 1 << 30, None)
+    assert ext(f) == pk.KV_ENOTSUP
+    assert ext(c, budget=0) == pk.KV_EINVAL
+    assert ext(c, mctx=1000, mb=16) == pk.KV_EINVAL   # table too narrow for the context
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_reorder_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 40))
+    q = rng.integers(0, 5, size=n) * rng.integers(0, 2, size=n) + rng.integers(0, 2, size=n)
+    c = rng.integers(0, 3, size=n) * rng.integers(0, 100, size=n)
+    for thr in (0, 1, 2):
+        perm, counts = pk.reorder_batch(q, c, thr)
+        operm, ocounts = obatch.reorder(q, c, thr)
+        assert perm == operm and counts == ocounts
+
+
+def test_reorder_rejects_negative_lengths():
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.reorder_batch([1, -2], [0, 0])
+    assert e.value.code == pk.KV_EINVAL

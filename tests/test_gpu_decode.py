@@ -1,0 +1,137 @@
+"""GPU parity: paged decode against the oracle (bf16 outputs within 1.5e-2,
+fp8-KV outputs within 5e-2, lse within 1e-3), plus poison, needle,
+split-invariance and determinism checks."""
+import numpy as np
+import pytest
+
+import paged_kv_cache_mapped_amd as pk
+from oracle import attention as oa, bf16 as ob, cache as oc
+from synth import workloads as w
+
+from .gpu_util import (BF16_TOL, FP8_TOL, LSE_TOL, bf16_to_f64, dev, device_cache, max_err,
+                       oracle_cache, say, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dc, st, split=0, max_seq_len=None):
+    msl = int(st.seq_lens.max()) if max_seq_len is None else max_seq_len
+    out, lse = pk.paged_decode(dc, dev(st.q), dev(st.block_tables), dev(st.seq_lens), msl,
+                               st.scale, split_tokens=split)
+    torch().cuda.synchronize()
+    return bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _check(st, ocache, out, lse, tol, rows=None):
+    rows = range(st.batch) if rows is None else rows
+    q = ob.to_f64(st.q)
+    for b in rows:
+        ro, rl = oa.paged_decode(q[b:b + 1], ocache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
+                                 st.scale)
+        e = max_err(out[b], ro[0])
+        el = max_err(lse[b], rl[0])
+        assert e <= tol, (b, e)
+        assert el <= LSE_TOL, (b, el)
+
+
+def test_tiny_decode_eight_steps():
+    """Batch 4, 8:2 heads, lengths in [100, 512]: eight steps of write-then-decode."""
+    st = w.tiny_decode()
+    rng = np.random.default_rng(101)
+    dc = device_cache(st.cache)
+    ocache = oracle_cache(st.cache)
+    for step in range(8):
+        say(f"tiny decode step {step} lens={st.seq_lens.tolist()}")
+        pk.kv_write(dc, dev(st.k_new), dev(st.v_new), dev(st.slot_mapping))
+        ocache = oc.write(ocache, st.k_new, st.v_new, st.slot_mapping)
+        out, lse = _run(dc, st)
+        _check(st, ocache, out, lse, BF16_TOL)
+        st = w.next_decode_step(rng, st)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 1), (32, 2), (40, 2), (12, 4)])
+@pytest.mark.parametrize("layout,dtype", [("nhd", "bf16"), ("nhd", "fp8"),
+                                          ("preshuffled", "bf16"), ("preshuffled", "fp8")])
+def test_decode_shapes_and_layouts(Hq, Hkv, layout, dtype):
+    st = w.decode_workload(5, 6, Hq, Hkv, 128, 16, 400, 1, 700, layout=layout, dtype=dtype,
+                           fixed_lens=[1, 15, 16, 33])  # edge lengths
+    w.poison_cache(st.cache, st.block_tables, st.seq_lens)
+    say(f"decode {layout} {dtype} {Hq}:{Hkv} lens={st.seq_lens.tolist()}")
+    dc = device_cache(st.cache)
+    tol = BF16_TOL if dtype == "bf16" else FP8_TOL
+    out, lse = _run(dc, st)
+    _check(st, oracle_cache(st.cache), out, lse, tol)
+
+
+@pytest.mark.parametrize("bs", [1, 4, 32, 64])
+def test_decode_block_sizes(bs):
+    st = w.decode_workload(6, 5, 16, 2, 128, bs, 5 * 900 // bs + 64, 1, 900)
+    w.poison_cache(st.cache, st.block_tables, st.seq_lens)
+    say(f"decode bs={bs}")
+    out, lse = _run(device_cache(st.cache), st)
+    _check(st, oracle_cache(st.cache), out, lse, BF16_TOL)
+
+
+def test_decode_split_invariance_and_determinism():
+    st = w.decode_workload(8, 4, 32, 4, 128, 16, 600, 1500, 2200)
+    dc = device_cache(st.cache)
+    ocache = oracle_cache(st.cache)
+    ref = None
+    for split in (0, 128, 256, 1024, 4096):
+        say(f"decode split={split}")
+        out, lse = _run(dc, st, split)
+        _check(st, ocache, out, lse, BF16_TOL)
+        out2, lse2 = _run(dc, st, split)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2)   # deterministic
+        if ref is not None:
+            assert max_err(out, ref[0]) <= 2 * BF16_TOL and max_err(lse, ref[1]) <= LSE_TOL
+        ref = (out, lse)
+
+
+def test_decode_needle():
+    """One planted key with a dominant score: the output must be its value row
+    (catches a mis-gathered block, which random data would hide)."""
+    st = w.decode_workload(9, 4, 8, 2, 128, 16, 700, 1000, 2500)
+    rng = np.random.default_rng(9)
+    k = st.cache.k
+    for b in range(st.batch):
+        L = int(st.seq_lens[b])
+        t = int(rng.integers(0, L))
+        blk, off = st.block_tables[b, t // 16], t % 16
+        for g in range(2):
+            qsum = ob.to_f64(st.q[b, 4 * g:4 * g + 4]).sum(0)
+            needle = 3.0 * qsum / np.linalg.norm(qsum) * np.sqrt(128)
+            k[blk, off, g] = w.f32_to_bf16_bits(needle.astype(np.float32))
+    say("decode needle")
+    out, lse = _run(device_cache(st.cache), st)
+    _check(st, oracle_cache(st.cache), out, lse, BF16_TOL)
+
+
+def test_decode_llama70b_full_size_sampled():
+    """Batch 64, 64:8 heads, lengths in [2048, 8192], 32768 blocks; every
+    output computed on the GPU, 6 requests checked against the oracle."""
+    st = w.llama70b_decode_layer()
+    say("decode llama70b full size")
+    dc = device_cache(st.cache)
+    pk.kv_write(dc, dev(st.k_new), dev(st.v_new), dev(st.slot_mapping))
+    ocache = oc.write(oracle_cache(st.cache), st.k_new, st.v_new, st.slot_mapping)
+    out, lse = _run(dc, st)
+    assert not np.isnan(out).any()
+    rows = list(np.random.default_rng(0).choice(st.batch, 6, replace=False))
+    rows += [int(np.argmax(st.seq_lens)), int(np.argmin(st.seq_lens))]
+    _check(st, ocache, out, lse, BF16_TOL, rows)
+
+
+def test_decode_fp8_preshuffled_full_size_sampled():
+    """Batch 128, 64:4 heads, lengths in [1000, 16000], fp8 e4m3 preshuffled
+    (x = 16), 131072 blocks; 6 requests checked against the oracle."""
+    st = w.fp8_preshuffled_decode()
+    say("decode fp8 preshuffled full size")
+    dc = device_cache(st.cache)
+    pk.kv_write(dc, dev(st.k_new), dev(st.v_new), dev(st.slot_mapping))
+    ocache = oc.write(oracle_cache(st.cache), st.k_new, st.v_new, st.slot_mapping)
+    out, lse = _run(dc, st)
+    assert not np.isnan(out).any()
+    rows = list(np.random.default_rng(1).choice(st.batch, 6, replace=False))
+    rows += [int(np.argmax(st.seq_lens))]
+    _check(st, ocache, out, lse, FP8_TOL, rows)
