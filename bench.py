@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  A step is one pass of the workload's whole hot path
+over one batch of seeded synthetic input that is already resident in HBM:
+
+  llama70b_decode_layer (default, the headline): Llama-3.1-70B-shaped decode
+      layer -- batch 64, 64 query : 8 KV heads, head_dim 128, bf16 NHD cache,
+      block 16, context lengths uniform in [2048, 8192], fully fragmented
+      tables.  Step = kv_write of the 64 new tokens + paged_decode + packing
+      all 5000 blocks of 8 requests x 10000 tokens (kv_pack_layer) + unpacking
+      them into a receiving cache (kv_unpack_layer).
+      value = algorithmic HBM bytes of the step / step time (GB/s).
+  qwen3_mixed_batch: Qwen3-235B-A22B-shaped mixed batch reordered
+      [decode:extend:prefill] -- 64:4 heads, 48 decodes (context [2000, 3000]),
+      4 extends (512 new on 2000 cached), 2 prefills of 2000, all causal.
+      Step = kv_write of all 6096 rows + paged_decode + extend_attn +
+      prefill_attn.  value = query tokens / step time (tokens/s).
+
+Roofline: the dominant call's algorithmic bytes (or flops) per launch divided
+by its average duration from HIP events recorded on the stream it runs on.
+cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+METRIC = "paged decode HBM GB/s (% of 8 TB/s); mixed-batch attention tokens/s"
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- workloads
+class Call:
+    """One library call of the step with its algorithmic cost per launch."""
+
+    def __init__(self, name, fn, bytes_=0.0, flops=0.0):
+        self.name, self.fn, self.bytes, self.flops = name, fn, float(bytes_), float(flops)
+
+
+def build_llama70b_decode_layer(torch, pk, w, dev):
+    st = w.llama70b_decode_layer()
+    job = w.pack_job(2, st.cache.spec.num_blocks)
+    sp = st.cache.spec
+    dc = pk.PagedKVCache(dev(st.cache.k), dev(st.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim)
+    recv = pk.PagedKVCache(torch.zeros_like(dc.k), torch.zeros_like(dc.v), sp.block_size,
+                           sp.num_kv_heads, sp.head_dim)
+    q, kn, vn = dev(st.q), dev(st.k_new), dev(st.v_new)
+    slots, tables, lens = dev(st.slot_mapping), dev(st.block_tables), dev(st.seq_lens)
+    msl = int(st.seq_lens.max())
+    B, Hq, D, Hkv = st.batch, st.num_q_heads, sp.head_dim, sp.num_kv_heads
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(pk.paged_decode_workspace_bytes(dc, B, Hq, msl), 16), dtype=torch.uint8,
+                     device=q.device)
+    src_ids, dst_ids = dev(job.src_ids), dev(job.dst_ids)
+    n = int(job.src_ids.size)
+    buf = torch.empty(pk.kv_layer_packed_bytes(dc, n), dtype=torch.uint8, device=q.device)
+
+    row = Hkv * D * 2
+    write_bytes = B * (2 * row * 2 + 8)
+    kv_bytes = float(st.seq_lens.astype(np.int64).sum()) * row * 2
+    blocks = float(((st.seq_lens + 15) // 16).sum())
+    decode_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4 + blocks * 4 + B * 4
+    decode_flops = float(st.seq_lens.astype(np.int64).sum()) * Hq * 4 * D
+    pack_bytes = 2.0 * buf.numel() + n * 4
+
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), write_bytes),
+        Call("paged_decode", lambda: pk.paged_decode(dc, q, tables, lens, msl, st.scale, out=out,
+                                                     lse=lse, workspace=ws),
+             decode_bytes, decode_flops),
+        Call("kv_pack_layer", lambda: pk.kv_pack_layer(dc, src_ids, buf), pack_bytes),
+        Call("kv_unpack_layer", lambda: pk.kv_unpack_layer(recv, dst_ids, buf), pack_bytes),
+    ]
+    config = {
+        "workload": "llama-3.1-70b decode layer: batch 64, 64:8 heads, head_dim 128, bf16 NHD "
+                    "cache, block 16, ctx U[2048,8192]; + pack/unpack of 5000 blocks "
+                    "(8 req x 10000 tokens, 327.68 MB)",
+        "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
+        "kv_tokens": int(st.seq_lens.sum()), "pack_blocks": n,
+    }
+
+    def cpu_sample(budget_s=12.0):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.Cache(st.cache.k, st.cache.v, "nhd", "bf16", 16, Hkv, D)
+        qf = ob.to_f64(st.q)
+        done_bytes, t0, nreq = 0.0, time.perf_counter(), 0
+        while time.perf_counter() - t0 < budget_s * 0.8:      # cycles over the batch
+            b = nreq % B
+            oa.paged_decode(qf[b:b + 1], ocache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
+                            st.scale)
+            done_bytes += float(st.seq_lens[b]) * row * 2 + 2 * Hq * D * 2
+            nreq += 1
+        m, npk = 500, 0
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < budget_s * 0.2:
+            buf_h = oc.pack_layer(ocache, job.src_ids[:m])
+            oc.unpack_layer(ocache, job.dst_ids[:m], buf_h)
+            done_bytes += 4.0 * buf_h.size
+            npk += 1
+        t2 = time.perf_counter()
+        return done_bytes / (t2 - t0) / 1e9, (
+            f"oracle decode of {nreq} requests of this batch (all 64 heads) + {npk} pack/unpack "
+            f"round trips of {m} of the {n} blocks; {t2 - t0:.1f} s")
+
+    return calls, "paged_decode", "hbm", config, cpu_sample, ("GB/s", None)
+
+
+def build_qwen3_mixed_batch(torch, pk, w, dev):
+    mb = w.qwen3_mixed_batch()
+    sp = mb.cache.spec
+    dc = pk.PagedKVCache(dev(mb.cache.k), dev(mb.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim)
+    q, kn, vn, slots = dev(mb.q), dev(mb.k_new), dev(mb.v_new), dev(mb.slot_mapping)
+    d0, d1 = mb.rows_decode
+    e0, e1 = mb.rows_extend
+    p0, p1 = mb.rows_prefill
+    Hq, Hkv, D = mb.num_q_heads, sp.num_kv_heads, sp.head_dim
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=q.device)
+    dtab, dlen = dev(mb.dec_tables), dev(mb.dec_seq_lens)
+    dmsl = int(mb.dec_seq_lens.max())
+    dws = torch.empty(max(pk.paged_decode_workspace_bytes(dc, d1 - d0, Hq, dmsl), 16),
+                      dtype=torch.uint8, device=q.device)
+    ecu, ectx, etab = dev(mb.ext_cu_q), dev(mb.ext_ctx), dev(mb.ext_tables)
+    E = int(mb.ext_ctx.size)
+    emq = int(np.diff(mb.ext_cu_q).max())
+    emc = int(mb.ext_ctx.max())
+    ews = torch.empty(max(pk.extend_attn_workspace_bytes(dc, E, e1 - e0, Hq, emc, 32768), 16),
+                      dtype=torch.uint8, device=q.device)
+    pcu = dev(mb.pre_cu)
+    pmax = int(np.diff(mb.pre_cu).max())
+    T = int(q.shape[0])
+
+    row = Hkv * D * 2
+    dec_bytes = float(mb.dec_seq_lens.astype(np.int64).sum()) * row * 2
+    ext_pairs = sum(int(n) * int(c) + int(n) * (int(n) + 1) // 2
+                    for n, c in zip(np.diff(mb.ext_cu_q), mb.ext_ctx))
+    pre_pairs = sum(int(n) * (int(n) + 1) // 2 for n in np.diff(mb.pre_cu))
+
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), T * (4 * row + 8)),
+        Call("paged_decode", lambda: pk.paged_decode(dc, q[d0:d1], dtab, dlen, dmsl, mb.scale,
+                                                     out=out[d0:d1], lse=lse[d0:d1], workspace=dws),
+             dec_bytes),
+        Call("extend_attn", lambda: pk.extend_attn(dc, q[e0:e1], kn[e0:e1], vn[e0:e1], ecu, ectx,
+                                                   etab, emq, emc, mb.scale, 32768, out=out[e0:e1],
+                                                   lse=lse[e0:e1], workspace=ews),
+             0.0, float(ext_pairs) * Hq * 4 * D),
+        Call("prefill_attn", lambda: pk.prefill_attn(q[p0:p1], kn[p0:p1], vn[p0:p1], pcu, pmax,
+                                                     mb.scale, True, out=out[p0:p1], lse=lse[p0:p1]),
+             0.0, float(pre_pairs) * Hq * 4 * D),
+    ]
+    config = {
+        "workload": "qwen3-235b-a22b mixed batch [decode:extend:prefill]: 64:4 heads, head_dim 128, "
+                    "bf16 NHD, block 16; 48 decodes ctx U[2000,3000], 4 extends 512 new on 2000 "
+                    "cached, 2 prefills of 2000; 6096 query tokens",
+        "query_tokens": T, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+    }
+
+    def cpu_sample(budget_s=12.0):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.write(oc.Cache(mb.cache.k, mb.cache.v, "nhd", "bf16", 16, Hkv, D),
+                          mb.k_new, mb.v_new, mb.slot_mapping)
+        qf = ob.to_f64(mb.q)
+        kf, vf = ob.to_f64(mb.k_new), ob.to_f64(mb.v_new)
+        t0 = time.perf_counter()
+        nd = npf = 0
+        while time.perf_counter() - t0 < budget_s:     # decode rows and prefill rows alternately
+            b = nd % (d1 - d0)
+            oa.paged_decode(qf[b:b + 1], ocache, mb.dec_tables[b:b + 1], mb.dec_seq_lens[b:b + 1],
+                            mb.scale)
+            nd += 1
+            r = (npf * 97) % (p1 - p0)
+            oa.prefill(qf[p0:p1], kf[p0:p1], vf[p0:p1], mb.pre_cu, mb.scale, rows=[r])
+            npf += 1
+        t2 = time.perf_counter()
+        return (nd + npf) / (t2 - t0), (f"oracle decode of {nd} decode rows + {npf} prefill rows "
+                                        f"of this batch (all 64 heads); {t2 - t0:.1f} s")
+
+    return calls, "prefill_attn", "mfma", config, cpu_sample, ("tokens/s", T)
+
+
+WORKLOADS = {
+    "llama70b_decode_layer": build_llama70b_decode_layer,
+    "qwen3_mixed_batch": build_qwen3_mixed_batch,
+}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama70b_decode_layer", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs its whole hot path on a single "
+              "MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_mapped_amd as pk
+    from synth import workloads as w
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pk.lib()
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    _log(f"building workload {args.workload}")
+    calls, dominant, bound, config, cpu_sample, (unit, tokens) = WORKLOADS[args.workload](
+        torch, pk, w, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for c in calls:
+            c.fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / max(args.steps, 1)
+
+    # per-call durations from HIP events on the stream the library launches on
+    stream = torch.cuda.current_stream()
+    per = {}
+    for c in calls:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            c.fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        avg = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        d = {"ms": round(avg, 5)}
+        if c.bytes:
+            d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
+            d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+        if c.flops:
+            d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
+            d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+        per[c.name] = d
+
+    dom = next(c for c in calls if c.name == dominant)
+    dms = per[dominant]["ms"]
+    if bound == "hbm":
+        ach = dom.bytes / (dms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = dom.flops / (dms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": None}
+
+    if unit == "GB/s":
+        value = sum(c.bytes for c in calls) / (ms * 1e-3) / 1e9
+    else:
+        value = tokens / (ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle on a sample")
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        v, sample = cpu_sample()
+        cpu = {"value": round(v, 4), "unit": unit, "cores": int(cores), "kind": "oracle",
+               "sample": sample}
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded numpy PCG64; no datasets or weights)",
+        "config": config, "roofline": roof, "cpu_baseline": cpu, "calls": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
