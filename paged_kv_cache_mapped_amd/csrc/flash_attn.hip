@@ -1,16 +1,495 @@
-// placeholder: prefill / extend kernels
+// Prefill and extend attention for gfx950: an MFMA flash-attention tile core.
+//
+// "Beyond just running: native inference optimisation in vLLM on AMD ROCm":
+// * section "Every batch handles a mixed workload": prefill is large matrix
+//   products (compute bound, wants big tiles and high ALU use); extend attends
+//   both to the cached context and to this round's new tokens;
+// * section "ROCM_AITER_FA": prefill runs a variable-length flash-attention
+//   kernel on the matrix cores; long contexts are processed in chunks under a
+//   per-iteration token budget (about 32K) shared by the extend requests and
+//   merged by log-sum-exp;
+// * section "Processing details of the three paths": prefill Q/K/V use the
+//   [num_tokens, num_heads, head_dim] layout; extend = (1) new tokens among
+//   themselves, (2) per context chunk: attention of the new tokens to the chunk
+//   and an LSE merge, (3) a final merge.  Each chunk yields an output and an
+//   LSE that records its softmax denominator.
+//
+// Tile core.  A workgroup of 4 waves owns 128 query rows of one query head
+// (32 rows per wave) and walks the key range in tiles of 64 keys staged in LDS
+// (double buffered: the next tile is loaded into registers while the current
+// one is consumed).  Per tile each wave computes
+//     S^T (64 keys x 32 rows) = K Q^T         16 x v_mfma_f32_32x32x16_bf16
+//     online softmax per row in registers     (a row's 64 scores live in two
+//                                              lanes: in-lane max/sum + one
+//                                              cross-lane exchange)
+//     O^T (128 dims x 32 rows) += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
+// Q^T stays in registers as the B operand; K rows are read from LDS as the A
+// operand; V^T comes out of the natural row-major V tile through
+// ds_read_b64_tr_b16 (transposing LDS read); P^T is the S^T accumulator
+// converted to bf16 in place (its lane layout already is the B-operand layout
+// once the 16 keys of an MFMA k-step are taken in the order the accumulator
+// holds them).  Scores are kept in the exp2 domain (scale * log2 e folded in).
+//
+// Keys are read either from contiguous [tokens, H_kv, D] tensors (prefill, and
+// the new tokens of an extend) or straight from the paged NHD cache through
+// the block table (extend context chunks) -- no gather copy.
 #include "common.h"
 #include "internal.h"
+
 namespace pkv {
-hipError_t launch_prefill(const void*, const void*, const void*, const int32_t*, int32_t, int32_t,
-                          int32_t, int32_t, float, int32_t, void*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBM = 128;                   // query rows per workgroup
+constexpr int kBN = 64;                    // keys per tile
+constexpr int kKRow = 272;                 // LDS bytes per K row (256 + 16 pad)
+constexpr int kVRow = 288;                 // LDS bytes per V row (256 + 32 pad)
+constexpr int kKTile = kBN * kKRow;
+constexpr int kVTile = kBN * kVRow;
+constexpr int kStage = kKTile + kVTile;    // 35840 bytes
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct AttnArgs {
+  const __bf16* q;          // [rows][Hq][D]
+  const __bf16* k;          // [rows][Hkv][D]  (prefill keys / extend new keys)
+  const __bf16* v;
+  const int32_t* cu;        // [num_seqs+1] row offsets
+  const uint8_t* kc;        // paged NHD cache (extend context)
+  const uint8_t* vc;
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  __bf16* out;
+  float* lse;
+  float* part_o;            // [n_parts][rows][Hq][D]
+  float* part_lse;          // [n_parts][rows][Hq]
+  int32_t max_blocks, num_blocks, bs, bs_log2;
+  int32_t Hq, Hkv, G, num_seqs, n_qtiles, n_parts, chunk_tokens, rows;
+  int64_t items;            // logical work items
+  int64_t grid_pad;         // launched workgroups (multiple of 8)
+  float qk_mult;            // scale * log2(e)
+};
+
+// Launched workgroup L runs on XCD L % 8.  Give each XCD a contiguous range of
+// the logical item order, so workgroups sharing a KV head (and its K/V tiles)
+// share that XCD's L2.
+__device__ __forceinline__ int64_t logical_item(const AttnArgs& a) {
+  const int64_t L = blockIdx.x;
+  return (L & 7) * (a.grid_pad >> 3) + (L >> 3);
 }
-ExtendPlan plan_extend(const kv_cache_t&, int32_t, int32_t, int32_t) { return ExtendPlan{16, 0, 1}; }
-size_t extend_workspace_bytes(const ExtendPlan&, int32_t, int32_t, int32_t) { return 0; }
-hipError_t launch_extend(const kv_cache_t&, const ExtendPlan&, const void*, const void*, const void*,
-                         const int32_t*, const int32_t*, const int32_t*, int32_t, int32_t, int32_t,
-                         int32_t, int32_t, float, void*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+
+struct KeySrc {
+  const uint8_t* kb;        // contiguous: K of key 0; paged: cache base
+  const uint8_t* vb;
+  const int32_t* trow;      // paged only
+  int32_t hkv;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t key_row_bytes(const AttnArgs& a, const KeySrc& s, int32_t key) {
+  if constexpr (PAGED) {
+    int32_t blk = s.trow[key >> a.bs_log2];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const int64_t slot = (int64_t)blk * a.bs + (key & (a.bs - 1));
+    return (slot * a.Hkv + s.hkv) * (kD * 2);
+  } else {
+    return ((int64_t)key * a.Hkv + s.hkv) * (kD * 2);
+  }
 }
+
+// Each thread stages rows tid/16 + 16*j (j = 0..3), 16-byte chunk tid%16, of
+// the K and V tiles; keys past k_end are clamped to the last key (finite data
+// whose probability is exactly zero).
+template <bool PAGED>
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const KeySrc& s, int32_t k0,
+                                          int32_t k_end, u32x4_t (&rk)[4], u32x4_t (&rv)[4]) {
+  const int c = threadIdx.x & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int32_t key = k0 + (threadIdx.x >> 4) + 16 * j;
+    key = key < k_end ? key : k_end - 1;
+    const int64_t off = key_row_bytes<PAGED>(a, s, key) + c * 16;
+    rk[j] = *(const u32x4_t*)(s.kb + off);
+    rv[j] = *(const u32x4_t*)(s.vb + off);
+  }
+}
+
+__device__ __forceinline__ void store_tile(uint8_t* stage, const u32x4_t (&rk)[4],
+                                           const u32x4_t (&rv)[4]) {
+  const int c = threadIdx.x & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (threadIdx.x >> 4) + 16 * j;
+    *(u32x4_t*)(stage + row * kKRow + c * 16) = rk[j];
+    *(u32x4_t*)(stage + kKTile + row * kVRow + c * 16) = rv[j];
+  }
+}
+
+// Attention of 128 query rows (rows q0.. of a sequence whose row 0 is global
+// row qbase) of head h against keys [k_begin, k_end).  CAUSAL: key j is visible
+// to row i iff j <= i.  Writes bf16 output + lse, or an fp32 partial.
+template <bool PAGED, bool CAUSAL, bool PARTIAL>
+__device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, int32_t h,
+                           int64_t qbase, int32_t q0, int32_t qn, int32_t k_begin, int32_t k_end,
+                           int32_t part) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
+  const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
+  const int32_t row = q0 + 32 * wave + r;       // this lane's query row (in sequence)
+  const int32_t wrow0 = q0 + 32 * wave;         // first row of this wave
+
+  // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
+  bf16x8_t qb[8];
+  {
+    const bf16x8_t zero = {};
+    const __bf16* qp = a.q + ((qbase + row) * a.Hq + h) * kD + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = row < qn ? *(const bf16x8_t*)(qp + 16 * ks) : zero;
+  }
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  // key range actually needed by this block
+  int32_t kend = k_end;
+  if constexpr (CAUSAL) {
+    const int32_t last_row = min(q0 + kBM, qn) - 1;
+    kend = min(kend, last_row + 1);
+  }
+  if (kend <= k_begin) return;               // never taken: callers pass a non-empty range
+  const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
+
+  u32x4_t rk[4], rv[4];
+  load_tile<PAGED>(a, src, k_begin, kend, rk, rv);
+  store_tile(smem, rk, rv);
+  __syncthreads();
+
+  for (int32_t t = 0; t < n_tiles; ++t) {
+    const int32_t k0 = k_begin + t * kBN;
+    uint8_t* st = smem + (t & 1) * kStage;
+    const bool more = t + 1 < n_tiles;
+    if (more) load_tile<PAGED>(a, src, k0 + kBN, kend, rk, rv);
+
+    // ---- S^T = K Q^T
+    f32x16_t s[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
+      const uint8_t* kp = st + (32 * ks2 + r) * kKRow + 16 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s[ks2] = mfma32(*(const bf16x8_t*)(kp + 32 * ks), qb[ks], s[ks2]);
+    }
+
+    // ---- scale, mask, online softmax (row = this lane's query row)
+    bool need_mask = k0 + kBN > kend;
+    if constexpr (CAUSAL) need_mask = need_mask || (k0 + kBN - 1 > wrow0);
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[ks2][i] *= a.qk_mult;
+    if (need_mask) {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int32_t key = k0 + 32 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          bool dead = key >= kend;
+          if constexpr (CAUSAL) dead = dead || key > row;
+          if (dead) s[ks2][i] = kNegInf;
+        }
+    }
+    float mt = s[0][0];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[ks2][i] = fast_exp2(s[ks2][i] - m_use);
+        psum += s[ks2][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+
+    // P^T as B operand: k-step kk covers keys 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
+
+    // ---- O^T += V^T P^T
+    const uint8_t* vt = st + kKTile;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int vrow = 16 * kk + 4 * (g16 >> 1) + (l16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int colb = (32 * dt + 16 * (g16 & 1) + 4 * (l16 & 3)) * 2;
+        const s16x4_t lo = lds_read_tr16(vt + vrow * kVRow + colb);
+        const s16x4_t hi = lds_read_tr16(vt + (vrow + 8) * kVRow + colb);
+        o[dt] = mfma32(cat_tr(lo, hi), pb[kk], o[dt]);
+      }
+    }
+
+    if (more) store_tile(smem + ((t + 1) & 1) * kStage, rk, rv);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  l_run += __shfl_xor(l_run, 32);
+  if (row >= qn) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  const int64_t grow = qbase + row;
+  if constexpr (PARTIAL) {
+    float* op = a.part_o + (((int64_t)part * a.rows + grow) * a.Hq + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4_t v4 = {o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv, o[dt][4 * i4 + 2] * inv,
+                            o[dt][4 * i4 + 3] * inv};
+        *(f32x4_t*)(op + 32 * dt + 8 * i4 + 4 * hh) = v4;
+      }
+    if (hh == 0) a.part_lse[((int64_t)part * a.rows + grow) * a.Hq + h] = lse_v;
+  } else {
+    __bf16* op = a.out + (grow * a.Hq + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const bf16x4_t v4 = {(__bf16)(o[dt][4 * i4] * inv), (__bf16)(o[dt][4 * i4 + 1] * inv),
+                             (__bf16)(o[dt][4 * i4 + 2] * inv), (__bf16)(o[dt][4 * i4 + 3] * inv)};
+        *(bf16x4_t*)(op + 32 * dt + 8 * i4 + 4 * hh) = v4;
+      }
+    if (hh == 0 && a.lse) a.lse[grow * a.Hq + h] = lse_v;
+  }
+}
+
+// Logical order: (seq, kv head, query head in group, query tile descending),
+// so heavy causal tiles start first and a KV head's tiles stay together.
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void prefill_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  const int64_t item = logical_item(a);
+  if (item >= a.items) return;
+  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
+  int64_t rest = item / a.n_qtiles;
+  const int32_t g = (int32_t)(rest % a.G);
+  rest /= a.G;
+  const int32_t hkv = (int32_t)(rest % a.Hkv);
+  const int32_t seq = (int32_t)(rest / a.Hkv);
+  const int32_t s0 = a.cu[seq];
+  const int32_t qn = a.cu[seq + 1] - s0;
+  const int32_t q0 = qt * kBM;
+  if (q0 >= qn) return;
+  KeySrc src;
+  src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
+  src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
+  src.trow = nullptr;
+  src.hkv = hkv;
+  attn_block<false, CAUSAL, false>(a, smem, src, hkv * a.G + g, s0, q0, qn, 0, qn, 0);
+}
+
+// Logical order: (seq, part, kv head, query head, query tile descending).
+// Part 0: the new tokens among themselves (causal).  Part p >= 1: the new
+// tokens against context chunk p-1 = cached tokens [(p-1)*chunk, p*chunk).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void extend_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  const int64_t item = logical_item(a);
+  if (item >= a.items) return;
+  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
+  int64_t rest = item / a.n_qtiles;
+  const int32_t g = (int32_t)(rest % a.G);
+  rest /= a.G;
+  const int32_t hkv = (int32_t)(rest % a.Hkv);
+  rest /= a.Hkv;
+  const int32_t part = (int32_t)(rest % a.n_parts);
+  const int32_t seq = (int32_t)(rest / a.n_parts);
+  const int32_t s0 = a.cu[seq];
+  const int32_t qn = a.cu[seq + 1] - s0;
+  const int32_t q0 = qt * kBM;
+  if (q0 >= qn) return;
+  const int32_t h = hkv * a.G + g;
+  if (part == 0) {
+    KeySrc src;
+    src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
+    src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
+    src.trow = nullptr;
+    src.hkv = hkv;
+    attn_block<false, true, true>(a, smem, src, h, s0, q0, qn, 0, qn, 0);
+  } else {
+    int32_t C = a.ctx_lens[seq];
+    const int32_t cap = a.max_blocks << a.bs_log2;
+    C = C > cap ? cap : C;
+    const int32_t kb = (part - 1) * a.chunk_tokens;
+    if (kb >= C) return;
+    const int32_t ke = min(C, kb + a.chunk_tokens);
+    KeySrc src;
+    src.kb = a.kc;
+    src.vb = a.vc;
+    src.trow = a.tables + (int64_t)seq * a.max_blocks;
+    src.hkv = hkv;
+    attn_block<true, false, true>(a, smem, src, h, s0, q0, qn, kb, ke, part);
+  }
+}
+
+// Final merge of the extend parts of each (row, head), one wave each:
+// o = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p - max_p lse_p),
+// lse = max + ln sum_p w_p.
+__global__ __launch_bounds__(256) void extend_merge_kernel(AttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
+  if (rh >= (int64_t)a.rows * a.Hq) return;
+  const int32_t grow = (int32_t)(rh / a.Hq);
+  // the request owning this row (cu is sorted)
+  int32_t lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.cu[mid] <= grow) lo = mid; else hi = mid - 1;
+  }
+  int32_t C = a.ctx_lens[lo];
+  const int32_t cap = a.max_blocks << a.bs_log2;
+  C = C > cap ? cap : C;
+  C = C < 0 ? 0 : C;
+  int32_t np = 1 + (C + a.chunk_tokens - 1) / a.chunk_tokens;
+  np = np > a.n_parts ? a.n_parts : np;
+  const int64_t stride = (int64_t)a.rows * a.Hq;
+  float M = kNegInf;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_lse[p * stride + rh]);
+  f32x2_t acc = {0.f, 0.f};
+  float wsum = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float lp = a.part_lse[p * stride + rh];
+    const float w = lp == kNegInf ? 0.f : fast_exp2((lp - M) * kLog2e);
+    wsum += w;
+    acc += w * *((const f32x2_t*)(a.part_o + (p * stride + rh) * kD) + lane);
+  }
+  const float inv = 1.f / wsum;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  *(bf16x2_t*)(a.out + rh * kD + 2 * lane) = bf16x2_t{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
+  if (lane == 0 && a.lse) a.lse[rh] = M + __log2f(wsum) * kLn2;
+}
+
+int32_t log2i(int32_t v) {
+  int32_t l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                          int32_t num_seqs, int32_t max_seqlen, int32_t num_q_heads,
+                          int32_t num_kv_heads, float scale, int32_t causal, void* out, float* lse,
+                          hipStream_t s) {
+  AttnArgs a = {};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k;
+  a.v = (const __bf16*)v;
+  a.cu = cu_seqlens;
+  a.out = (__bf16*)out;
+  a.lse = lse;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.G = num_q_heads / num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.n_qtiles = (max_seqlen + kBM - 1) / kBM;
+  a.n_parts = 1;
+  a.qk_mult = scale * kLog2e;
+  a.items = (int64_t)num_seqs * num_q_heads * a.n_qtiles;
+  a.grid_pad = (a.items + 7) & ~(int64_t)7;
+  if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
+  if (causal)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t max_ctx_len,
+                       int32_t chunk_budget_tokens) {
+  ExtendPlan p;
+  // Per-request share of the budget, rounded down to whole key tiles and
+  // blocks (at least one).
+  const int32_t unit = c.block_size > kBN ? c.block_size : kBN;
+  int64_t share = num_seqs > 0 ? (int64_t)chunk_budget_tokens / num_seqs : chunk_budget_tokens;
+  share = share / unit * unit;
+  if (share < unit) share = unit;
+  if (share > (1 << 30)) share = 1 << 30;
+  p.chunk_tokens = (int32_t)share;
+  p.n_chunks = max_ctx_len > 0 ? (int32_t)((max_ctx_len + share - 1) / share) : 0;
+  p.n_parts = p.n_chunks + 1;
+  return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
+                              int32_t head_dim) {
+  const size_t rows = (size_t)p.n_parts * total_new * num_q_heads;
+  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,
+                         const void* k_new, const void* v_new, const int32_t* cu_q_lens,
+                         const int32_t* ctx_lens, const int32_t* tables, int32_t max_blocks,
+                         int32_t num_seqs, int32_t total_new, int32_t max_q_len,
+                         int32_t num_q_heads, float scale, void* out, float* lse,
+                         void* workspace, hipStream_t s) {
+  AttnArgs a = {};
+  a.q = (const __bf16*)q;
+  a.k = (const __bf16*)k_new;
+  a.v = (const __bf16*)v_new;
+  a.cu = cu_q_lens;
+  a.kc = (const uint8_t*)c.k_cache;
+  a.vc = (const uint8_t*)c.v_cache;
+  a.tables = tables;
+  a.ctx_lens = ctx_lens;
+  a.out = (__bf16*)out;
+  a.lse = lse;
+  const size_t prow = (size_t)p.n_parts * total_new * num_q_heads;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((uint8_t*)workspace + align256(prow * c.head_dim * sizeof(float)));
+  a.max_blocks = max_blocks > 0 ? max_blocks : 1;
+  a.num_blocks = c.num_blocks;
+  a.bs = c.block_size;
+  a.bs_log2 = log2i(c.block_size);
+  a.Hq = num_q_heads;
+  a.Hkv = c.num_kv_heads;
+  a.G = num_q_heads / c.num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.n_qtiles = (max_q_len + kBM - 1) / kBM;
+  a.n_parts = p.n_parts;
+  a.chunk_tokens = p.chunk_tokens;
+  a.rows = total_new;
+  a.qk_mult = scale * kLog2e;
+  a.items = (int64_t)num_seqs * p.n_parts * num_q_heads * a.n_qtiles;
+  a.grid_pad = (a.items + 7) & ~(int64_t)7;
+  if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(extend_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rh = (int64_t)total_new * num_q_heads;
+  hipLaunchKernelGGL(extend_merge_kernel, dim3((unsigned)((rh + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

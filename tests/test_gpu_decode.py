@@ -25,6 +25,7 @@ def _run(dc, st, split=0, max_seq_len=None):
 def _check(st, ocache, out, lse, tol, rows=None):
     rows = range(st.batch) if rows is None else rows
     q = ob.to_f64(st.q)
+    worst = [0.0, 0.0]
     for b in rows:
         ro, rl = oa.paged_decode(q[b:b + 1], ocache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
                                  st.scale)
@@ -32,6 +33,8 @@ def _check(st, ocache, out, lse, tol, rows=None):
         el = max_err(lse[b], rl[0])
         assert e <= tol, (b, e)
         assert el <= LSE_TOL, (b, el)
+        worst = [max(worst[0], e), max(worst[1], el)]
+    say(f"  max|err| out {worst[0]:.3e} lse {worst[1]:.3e} over {len(list(rows))} requests")
 
 
 def test_tiny_decode_eight_steps():
