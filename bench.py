@@ -200,7 +200,50 @@ def build_qwen3_mixed_batch(torch, pk, w, dev):
     return calls, "prefill_attn", "mfma", config, cpu_sample, ("tokens/s", T)
 
 
+def build_long_context_extend(torch, pk, w, dev):
+    mb = w.long_context_extend()
+    sp = mb.cache.spec
+    dc = pk.PagedKVCache(dev(mb.cache.k), dev(mb.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim)
+    q, kn, vn, slots = dev(mb.q), dev(mb.k_new), dev(mb.v_new), dev(mb.slot_mapping)
+    Hq, Hkv, D = mb.num_q_heads, sp.num_kv_heads, sp.head_dim
+    T = int(q.shape[0])
+    E = int(mb.ext_ctx.size)
+    emq, emc = int(np.diff(mb.ext_cu_q).max()), int(mb.ext_ctx.max())
+    ws = torch.empty(max(pk.extend_attn_workspace_bytes(dc, E, T, Hq, emc, 32768), 16),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    ecu, ectx, etab = dev(mb.ext_cu_q), dev(mb.ext_ctx), dev(mb.ext_tables)
+    pairs = sum(int(n) * int(c) + int(n) * (int(n) + 1) // 2
+                for n, c in zip(np.diff(mb.ext_cu_q), mb.ext_ctx))
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), T * (4 * Hkv * D * 2 + 8)),
+        Call("extend_attn", lambda: pk.extend_attn(dc, q, kn, vn, ecu, ectx, etab, emq, emc,
+                                                   mb.scale, 32768, out=out, lse=lse, workspace=ws),
+             0.0, float(pairs) * Hq * 4 * D),
+    ]
+    config = {"workload": "long-context extend: 2 requests x (100000 cached + 8192 new), 64:8 heads, "
+                          "head_dim 128, bf16 NHD, block 16, 32768-token chunk budget",
+              "query_tokens": T}
+
+    def cpu_sample(budget_s=12.0):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.Cache(mb.cache.k, mb.cache.v, "nhd", "bf16", 16, Hkv, D)
+        qf, kf, vf = ob.to_f64(mb.q), ob.to_f64(mb.k_new), ob.to_f64(mb.v_new)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < budget_s:
+            oa.extend(qf, kf, vf, mb.ext_cu_q, mb.ext_ctx, ocache, mb.ext_tables, mb.scale,
+                      rows=[(n * 997) % T])
+            n += 1
+        return n / (time.perf_counter() - t0), f"oracle extend of {n} rows (all 64 heads)"
+
+    return calls, "extend_attn", "mfma", config, cpu_sample, ("tokens/s", T)
+
+
 WORKLOADS = {
+    "long_context_extend": build_long_context_extend,
     "llama70b_decode_layer": build_llama70b_decode_layer,
     "qwen3_mixed_batch": build_qwen3_mixed_batch,
 }
@@ -214,6 +257,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama70b_decode_layer", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the mixed-batch measurement that follows the headline workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs its whole hot path on a single "
@@ -232,75 +277,92 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    _log(f"building workload {args.workload}")
-    calls, dominant, bound, config, cpu_sample, (unit, tokens) = WORKLOADS[args.workload](
-        torch, pk, w, dev)
-    torch.cuda.synchronize()
-
-    def step():
-        for c in calls:
-            c.fn()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    _log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / max(args.steps, 1)
-
-    # per-call durations from HIP events on the stream the library launches on
-    stream = torch.cuda.current_stream()
-    per = {}
-    for c in calls:
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in evs:
-            a.record(stream)
-            c.fn()
-            b.record(stream)
+    def measure(name, with_cpu):
+        _log(f"building workload {name}")
+        calls, dominant, bound, config, cpu_sample, (unit, tokens) = WORKLOADS[name](
+            torch, pk, w, dev)
         torch.cuda.synchronize()
-        avg = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-        d = {"ms": round(avg, 5)}
-        if c.bytes:
-            d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
-            d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
-        if c.flops:
-            d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
-            d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
-        per[c.name] = d
 
-    dom = next(c for c in calls if c.name == dominant)
-    dms = per[dominant]["ms"]
-    if bound == "hbm":
-        ach = dom.bytes / (dms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        ach = dom.flops / (dms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": None}
+        def step():
+            for c in calls:
+                c.fn()
 
-    if unit == "GB/s":
-        value = sum(c.bytes for c in calls) / (ms * 1e-3) / 1e9
-    else:
-        value = tokens / (ms * 1e-3)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        _log(f"timing {args.steps} steps of {name}")
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / max(args.steps, 1)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        _log("timing the CPU oracle on a sample")
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            cores = os.cpu_count() or 1
-        v, sample = cpu_sample()
-        cpu = {"value": round(v, 4), "unit": unit, "cores": int(cores), "kind": "oracle",
-               "sample": sample}
+        # per-call durations from HIP events on the stream the library launches on
+        stream = torch.cuda.current_stream()
+        per = {}
+        for c in calls:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a, b in evs:
+                a.record(stream)
+                c.fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            avg = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+            d = {"ms": round(avg, 5)}
+            if c.bytes:
+                d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
+                d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+            if c.flops:
+                d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
+                d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+            per[c.name] = d
+
+        dom = next(c for c in calls if c.name == dominant)
+        dms = per[dominant]["ms"]
+        if bound == "hbm":
+            ach = dom.bytes / (dms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": None}
+        else:
+            ach = dom.flops / (dms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1),
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+        if unit == "GB/s":
+            value = sum(c.bytes for c in calls) / (ms * 1e-3) / 1e9
+        else:
+            value = tokens / (ms * 1e-3)
+        cpu = None
+        if with_cpu:
+            _log("timing the CPU oracle on a sample")
+            try:
+                from threadpoolctl import threadpool_info
+                cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            except Exception:
+                cores = os.cpu_count() or 1
+            v, sample = cpu_sample()
+            cpu = {"value": round(v, 4), "unit": unit, "cores": int(cores), "kind": "oracle",
+                   "sample": sample}
+        # free this workload's device memory before the next one
+        del calls
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return {"value": value, "unit": unit, "ms": ms, "config": config, "roofline": roof,
+                "calls": per, "cpu": cpu}
+
+    main_r = measure(args.workload, not args.no_cpu_baseline)
+    secondary = {}
+    if args.workload == "llama70b_decode_layer" and not args.no_secondary:
+        r = measure("qwen3_mixed_batch", False)
+        secondary["qwen3_mixed_batch"] = {
+            "metric": "mixed-batch attention tokens/s", "value": round(r["value"], 1),
+            "unit": r["unit"], "ms_per_step": round(r["ms"], 4), "config": r["config"],
+            "roofline": r["roofline"], "calls": r["calls"]}
+    value, unit, ms, config = main_r["value"], main_r["unit"], main_r["ms"], main_r["config"]
+    roof, per, cpu = main_r["roofline"], main_r["calls"], main_r["cpu"]
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -308,6 +370,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded numpy PCG64; no datasets or weights)",
         "config": config, "roofline": roof, "cpu_baseline": cpu, "calls": per,
+        "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
 
