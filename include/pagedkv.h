@@ -126,8 +126,13 @@ int kv_write(const kv_cache_t* cache, const void* k, const void* v,
  *   out           [batch][num_q_heads][head_dim] bf16
  *   lse           [batch][num_q_heads] fp32 or NULL
  *   workspace     >= paged_decode_workspace_bytes(...) bytes, 16-byte aligned
- * Split-K over fixed-size token ranges, combined by log-sum-exp weights
- * ([ROCm] section "Processing details of the three paths", LSE merge).
+ * Balanced split-K: the requests' token streams are concatenated and cut into
+ * equal pieces (a small on-device planning pass reads seq_lens), so every
+ * workgroup reads the same amount of KV; requests spanning several pieces are
+ * combined by log-sum-exp weights ([ROCm] section "Processing details of the
+ * three paths", LSE merge).  Lengths above max_seq_len or the table capacity
+ * are clamped; a request of length 0 leaves its output unwritten;
+ * batch * max_seq_len must stay below 2^31.
  * Layouts/dtypes: NHD bf16, NHD fp8, PRESHUFFLED bf16, PRESHUFFLED fp8.
  * num_q_heads must be a multiple of num_kv_heads.
  * ------------------------------------------------------------------------- */
@@ -139,8 +144,9 @@ int paged_decode(const kv_cache_t* cache, const void* q, int32_t batch,
                  int32_t max_seq_len, float scale, void* out, float* lse,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Same call with an explicit split size (tokens per split, a multiple of 128;
- * 0 = automatic), for tuning and for split-invariance tests. */
+/* Same call with an explicit piece length (split_tokens: a multiple of 32 up
+ * to 16384, clamped to what the LDS block-table slice holds; 0 = automatic),
+ * for tuning and for split-invariance tests. */
 size_t paged_decode_workspace_bytes_ex(const kv_cache_t* cache, int32_t batch,
                                        int32_t num_q_heads, int32_t max_seq_len,
                                        int32_t split_tokens);

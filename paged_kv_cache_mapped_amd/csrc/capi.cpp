@@ -101,10 +101,12 @@ static int decode_checks(const kv_cache_t* cache, int32_t batch, int32_t num_q_h
   if (st) return st;
   if (batch <= 0 || batch > 65535) return fail(KV_EINVAL, "%s: batch must be in [1, 65535]", fn);
   if (max_seq_len <= 0) return fail(KV_EINVAL, "%s: max_seq_len must be > 0", fn);
-  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 65536)
-    return fail(KV_EINVAL, "%s: split_tokens must be 0 or a multiple of 128 up to 65536", fn);
+  if (split_tokens < 0 || split_tokens % 32 != 0 || split_tokens > 16384)
+    return fail(KV_EINVAL, "%s: split_tokens must be 0 or a multiple of 32 up to 16384", fn);
   if ((num_q_heads / cache->num_kv_heads + 15) / 16 * cache->num_kv_heads > 65535)
     return fail(KV_EINVAL, "%s: too many heads", fn);
+  if ((int64_t)batch * (((int64_t)max_seq_len + 31) & ~(int64_t)31) >= ((int64_t)1 << 31))
+    return fail(KV_EINVAL, "%s: batch * max_seq_len must stay below 2^31", fn);
   return KV_OK;
 }
 
@@ -142,16 +144,13 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32
   if (!(scale > 0.f) && !(scale < 0.f) && scale != 0.f) return fail(KV_EINVAL, "%s: scale is NaN", fn);
   const pkv::DecodePlan p = pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens);
   const size_t need = pkv::decode_workspace_bytes(p, batch, num_q_heads, cache->head_dim);
-  if (p.n_splits > 1) {
-    if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
-    if (workspace_bytes < need)
-      return fail(KV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(KV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  }
-  if (p.n_splits > 2147483647 / 2) return fail(KV_EINVAL, "%s: too many splits", fn);
+  if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(KV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(KV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   return hip_status(pkv::launch_decode(*cache, p, q, batch, num_q_heads, block_tables,
-                                       max_blocks_per_seq, seq_lens, scale, out, lse, workspace,
-                                       (hipStream_t)stream),
+                                       max_blocks_per_seq, seq_lens, max_seq_len, scale, out, lse,
+                                       workspace, (hipStream_t)stream),
                     fn);
 }
 

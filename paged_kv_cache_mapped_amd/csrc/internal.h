@@ -19,9 +19,14 @@ hipError_t launch_pack(const kv_cache_t& c, const int32_t* ids, int32_t n, void*
 
 // ----------------------------------------------------------------- decode
 struct DecodePlan {
-  int32_t split_tokens;   // tokens per split, multiple of 128
-  int32_t n_splits;       // splits of the longest request
-  int32_t n_gchunks;      // ceil(G / 16) groups of query heads per KV head
+  int32_t split_tokens;      // fixed piece length requested by the caller (0 = automatic)
+  int32_t n_splits;          // = n_slots
+  int32_t n_gchunks;         // ceil(G / 16) groups of query heads per KV head
+  int32_t fixed_len;         // piece length if fixed, else 0
+  int32_t len_min, len_max;  // bounds of the automatic piece length
+  int32_t pieces_per_group;  // grid x: workgroups per (KV head, query-head group)
+  int32_t n_slots;           // partial slots per (request, head)
+  int32_t max_pieces;        // upper bound of the number of pieces
 };
 DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t split_tokens);
@@ -29,8 +34,8 @@ size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_
                               int32_t head_dim);
 hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
                          int32_t batch, int32_t num_q_heads, const int32_t* tables,
-                         int32_t max_blocks, const int32_t* seq_lens, float scale,
-                         void* out, float* lse, void* workspace, hipStream_t s);
+                         int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, void* out, float* lse, void* workspace, hipStream_t s);
 
 // ----------------------------------------------------------------- prefill / extend
 hipError_t launch_prefill(const void* q, const void* k, const void* v,

@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kVRowBytes = 288;                  // 128 bf16 + 32 B pad (bank spread)
 constexpr int kVTileBytes = kTile * kVRowBytes;  // per wave; also holds 16x128 fp32 at the end
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kTabCap = 512;                     // block ids of one split staged in LDS
 
 struct DecodeArgs {
   const uint8_t* kc;
@@ -52,10 +53,14 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   __bf16* out;
   float* lse;
-  float* part_o;
-  float* part_lse;
+  float* part_o;              // [B][Hq][n_slots][D]
+  float* part_lse;            // [B][Hq][n_slots]
+  int32_t* hdr;               // [0] padded total T, [1] piece length, [2] pieces
+  int32_t* cum;               // [B+1] exclusive prefix sums of lengths rounded up to 32
+  int32_t* first_seq;         // [max_pieces] first request touched by each piece
   int32_t max_blocks, num_blocks, bs, bs_log2, Hkv, Hq, G, n_gchunks;
-  int32_t split_tokens, n_splits, batch;
+  int32_t n_slots, batch, fixed_len, len_min, len_max, target_pieces;
+  int32_t max_len;            // lengths are clamped to min(table capacity, max_seq_len)
   float qk_mult;   // scale * k_scale * log2(e): scores in the exp2 domain
   float v_scale;
 };
@@ -73,276 +78,425 @@ __device__ __forceinline__ int dmap(int kk, int q4) {
   else return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
 }
 
+// Raw bytes of one wave's 32-token tile, as loaded (fp8 uses the low halves).
+struct TileRaw {
+  u32x4_t k[8];
+  u32x4_t v[8];
+};
+
+// Issue every load of the tile starting at token t0.  Tokens at or past t_end
+// are clamped to t_end - 1: their addresses stay inside the request and they
+// repeat a row already being fetched (cache hits), so tiles past the end can be
+// prefetched unconditionally.
 template <int LAYOUT, int DT>
-__device__ __forceinline__ void load_k(const DecodeArgs& a, const int32_t* trow, int hkv,
-                                       int32_t tok, int q4, bf16x8_t (&ka)[4]) {
-  const int32_t blk = clamp_block(trow[tok >> a.bs_log2], a.num_blocks);
-  const int32_t off = tok & (a.bs - 1);
-  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-    const int64_t row = ((int64_t)blk * a.bs + off) * a.Hkv + hkv;
-    if constexpr (DT == KV_DTYPE_BF16) {
-      const uint8_t* p = a.kc + row * (kD * 2);
+__device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s_tab, int32_t ib0,
+                                           int hkv, int32_t t0, int32_t t_end, int lane,
+                                           TileRaw& R) {
+  const int q4 = lane >> 4, r = lane & 15;
+  // K: A-operand rows = tokens t0 + 8*(r/4) + 4*s + r%4 (subtile s)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[kk] = *(const bf16x8_t*)(p + dmap<DT>(kk, q4) * 2);
+  for (int s = 0; s < 2; ++s) {
+    const int32_t tok = min(t0 + 8 * (r >> 2) + 4 * s + (r & 3), t_end - 1);
+    const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+    const int32_t off = tok & (a.bs - 1);
+    if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+      const int64_t row = ((int64_t)blk * a.bs + off) * a.Hkv + hkv;
+      if constexpr (DT == KV_DTYPE_BF16) {
+        const uint8_t* p = a.kc + row * (kD * 2);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) R.k[4 * s + kk] = *(const u32x4_t*)(p + dmap<DT>(kk, q4) * 2);
+      } else {
+        const uint8_t* p = a.kc + row * kD;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) R.k[2 * s + pp] = *(const u32x4_t*)(p + 16 * (4 * pp + q4));
+      }
     } else {
-      const uint8_t* p = a.kc + row * kD;
+      const int64_t bh = (int64_t)blk * a.Hkv + hkv;
+      if constexpr (DT == KV_DTYPE_BF16) {   // [blk][h][D/8][bs][8]
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const u32x4_t w = *(const u32x4_t*)(p + 16 * (4 * pp + q4));
-        ka[2 * pp] = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
-        ka[2 * pp + 1] = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t e = ((bh * (kD / 8) + (4 * kk + q4)) * a.bs + off) * 8;
+          R.k[4 * s + kk] = *(const u32x4_t*)(a.kc + e * 2);
+        }
+      } else {                                // [blk][h][D/16][bs][16]
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int64_t e = ((bh * (kD / 16) + (4 * pp + q4)) * a.bs + off) * 16;
+          R.k[2 * s + pp] = *(const u32x4_t*)(a.kc + e);
+        }
+      }
+    }
+  }
+  // V: NHD rows as 16-byte chunks of whole rows (row 4*j4 + lane/16, chunk
+  // lane%16); preshuffled V as the V^T operand (8 tokens of dim 16n + r).
+  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    const int a4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int j4 = 0; j4 < 8; ++j4) {
+      const int32_t tok = min(t0 + 4 * j4 + a4, t_end - 1);
+      const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+      const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
+      if constexpr (DT == KV_DTYPE_BF16) {
+        R.v[j4] = *(const u32x4_t*)(a.vc + row * (kD * 2) + c16 * 16);
+      } else {
+        const u32x2_t c = *(const u32x2_t*)(a.vc + row * kD + c16 * 8);
+        R.v[j4] = u32x4_t{c[0], c[1], 0u, 0u};
       }
     }
   } else {
-    const int64_t bh = (int64_t)blk * a.Hkv + hkv;
-    if constexpr (DT == KV_DTYPE_BF16) {   // [blk][h][D/8][bs][8]
+    constexpr int X = (DT == KV_DTYPE_BF16) ? 8 : 16;
+    const int32_t tb = min(t0 + 8 * q4, (t_end - 1) & ~7);   // 8 tokens, aligned to 8
+    const int32_t blk = s_tab[(tb >> a.bs_log2) - ib0];
+    const int32_t off = tb & (a.bs - 1);
+    const int64_t base = (((int64_t)blk * a.Hkv + hkv) * (a.bs / X) + off / X) * kD;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int64_t e = ((bh * (kD / 8) + (4 * kk + q4)) * a.bs + off) * 8;
-        ka[kk] = *(const bf16x8_t*)(a.kc + e * 2);
-      }
-    } else {                                // [blk][h][D/16][bs][16]
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int64_t e = ((bh * (kD / 16) + (4 * pp + q4)) * a.bs + off) * 16;
-        const u32x4_t w = *(const u32x4_t*)(a.kc + e);
-        ka[2 * pp] = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
-        ka[2 * pp + 1] = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+    for (int n = 0; n < 8; ++n) {
+      const int64_t e = (base + 16 * n + r) * X + (off % X);
+      if constexpr (DT == KV_DTYPE_BF16) {
+        R.v[n] = *(const u32x4_t*)(a.vc + e * 2);
+      } else {
+        const u32x2_t c = *(const u32x2_t*)(a.vc + e);
+        R.v[n] = u32x4_t{c[0], c[1], 0u, 0u};
       }
     }
   }
 }
 
+// Running state of one wave: O^T accumulators (element i of o[n] is dim
+// 16n + 4*q4 + i of query head r) and the exp2-domain max / lane-partial sum.
+struct WaveState {
+  f32x4_t o[8];
+  float m, l;
+};
+
 template <int LAYOUT, int DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3)))
-void decode_split_kernel(DecodeArgs a) {
-  const int32_t split = blockIdx.x;
-  const int32_t b = blockIdx.z;
+__device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw& R,
+                                             const bf16x8_t (&qb)[4], int32_t t0, int32_t t_end,
+                                             int lane, uint8_t* vt, WaveState& st) {
+  const int q4 = lane >> 4, r = lane & 15;
+  const bool partial = t0 + kTile > t_end;
+  bf16x8_t ka[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if constexpr (DT == KV_DTYPE_BF16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[s][kk] = __builtin_bit_cast(bf16x8_t, R.k[4 * s + kk]);
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const u32x4_t w = R.k[2 * s + pp];
+        ka[s][2 * pp] = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
+        ka[s][2 * pp + 1] = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+      }
+    }
+  }
+  bf16x8_t va[8];
+  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    const int a4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int j4 = 0; j4 < 8; ++j4) {
+      u32x4_t w = R.v[j4];
+      if constexpr (DT != KV_DTYPE_BF16)
+        w = __builtin_bit_cast(u32x4_t, fp8x8_to_bf16(u32x2_t{w[0], w[1]}));
+      *(u32x4_t*)(vt + (4 * j4 + a4) * kVRowBytes + c16 * 16) = w;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if constexpr (DT == KV_DTYPE_BF16) va[n] = __builtin_bit_cast(bf16x8_t, R.v[n]);
+      else va[n] = fp8x8_to_bf16(u32x2_t{R.v[n][0], R.v[n][1]});
+    }
+    if (partial) {
+      const int32_t tv = t0 + 8 * q4;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (tv + jj >= t_end) {
+#pragma unroll
+          for (int n = 0; n < 8; ++n) va[n][jj] = (__bf16)0.f;
+        }
+    }
+  }
+
+  // ---- S^T = K Q^T: element i of acc[s] is token t0 + 8*q4 + 4*s + i, head r
+  f32x4_t acc[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc[s] = mfma16(ka[s][kk], qb[kk], acc[s]);
+  }
+  float sc[8];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t tok = t0 + 8 * q4 + 4 * s + i;
+      sc[4 * s + i] = (partial && tok >= t_end) ? kNegInf : acc[s][i] * a.qk_mult;
+    }
+
+  // ---- online softmax for query head r (exp2 domain)
+  float mt = sc[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float m_new = fmaxf(st.m, mt);      // finite: every tile has a valid token
+  const float alpha = fast_exp2(st.m - m_new);
+  float p[8], psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(sc[i] - m_new);
+    psum += p[i];
+  }
+  st.l = st.l * alpha + psum;               // lane-partial; reduced at the end
+  st.m = m_new;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+  const bf16x8_t pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
+                       (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
+
+  // ---- O^T += V^T P^T
+  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    order_lds();
+    const int row0 = 8 * q4 + (r >> 2);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int colb = (16 * n + 4 * (r & 3)) * 2;
+      const s16x4_t lo = lds_read_tr16(vt + row0 * kVRowBytes + colb);
+      const s16x4_t hi = lds_read_tr16(vt + (row0 + 4) * kVRowBytes + colb);
+      st.o[n] = mfma16(cat_tr(lo, hi), pb, st.o[n]);
+    }
+    order_lds();
+  } else {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = mfma16(va[n], pb, st.o[n]);
+  }
+}
+
+__device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t cap) {
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// Work plan (one workgroup): lengths rounded up to the 32-token tile are
+// concatenated into one token stream of length T; the stream is cut into
+// pieces of equal length (a multiple of 32), so every workgroup of the main
+// kernel gets the same amount of KV to read however the lengths are spread.
+// Writes cum[] (exclusive prefix sums), the header and, for every piece, the
+// first request it touches.
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int32_t s_part[1024];
+  const int tid = threadIdx.x;
+  const int32_t B = a.batch;
+  const int32_t cap = a.max_len;
+  const int32_t per = (B + 1023) / 1024;
+  const int32_t b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int32_t sum = 0;
+  for (int32_t b = b0; b < b1; ++b) sum += (clamp_len(a.seq_lens[b], cap) + 31) & ~31;
+  s_part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {       // inclusive scan
+    const int32_t v = tid >= off ? s_part[tid - off] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid ? s_part[tid - 1] : 0;
+  for (int32_t b = b0; b < b1; ++b) {
+    a.cum[b] = run;
+    run += (clamp_len(a.seq_lens[b], cap) + 31) & ~31;
+  }
+  const int32_t T = s_part[1023];
+  int32_t len;
+  if (a.fixed_len > 0) {
+    len = a.fixed_len;
+  } else {
+    len = (T + a.target_pieces - 1) / a.target_pieces;
+    len = (len + 31) & ~31;
+    len = len < a.len_min ? a.len_min : (len > a.len_max ? a.len_max : len);
+  }
+  const int32_t NP = (T + len - 1) / len;
+  if (tid == 0) {
+    a.cum[B] = T;
+    a.hdr[0] = T;
+    a.hdr[1] = len;
+    a.hdr[2] = NP;
+  }
+  __threadfence();
+  __syncthreads();
+  // first request of piece p: the largest b with cum[b] <= p*len (empty
+  // requests share their successor's offset, so the largest one is non-empty)
+  const volatile int32_t* cum = a.cum;
+  for (int32_t p = tid; p < NP; p += 1024) {
+    const int32_t start = p * len;
+    int32_t lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= start) lo = mid; else hi = mid - 1;
+    }
+    a.first_seq[p] = lo;
+  }
+}
+
+// Main pass: workgroup (p, group) walks pieces p, p + gridDim.x, ... of the
+// token stream for its (KV head, query-head group); inside a piece it runs
+// one segment per request it overlaps.  Each segment ends with a 4-wave merge
+// and either the final output (a request covered by one piece) or an fp32
+// partial (o, lse) in slot (piece - first piece of the request).
+template <int LAYOUT, int DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void decode_piece_kernel(DecodeArgs a) {
   const int32_t hkv = blockIdx.y / a.n_gchunks;
   const int32_t gc = blockIdx.y - hkv * a.n_gchunks;
-  int32_t L = a.seq_lens[b];
-  const int32_t cap = a.max_blocks << a.bs_log2;
-  L = L > cap ? cap : L;
-  const int32_t t_begin = split * a.split_tokens;
-  if (t_begin >= L) return;                 // uniform over the workgroup
-  const int32_t t_end = min(L, t_begin + a.split_tokens);
-  const int32_t n_b = (L + a.split_tokens - 1) / a.split_tokens;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, r = lane & 15;
   const int g0 = gc * 16;
   const int gcnt = min(16, a.G - g0);
   const int32_t h_base = hkv * a.G + g0;
+  const int32_t cap = a.max_len;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * kVTileBytes];
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
+  __shared__ int32_t s_tab[kTabCap];
   uint8_t* vt = smem + wave * kVTileBytes;
 
-  // Q^T as the B operand: lane (q4, r) holds q[h_base + r][dmap(kk, q4) .. +8]
-  bf16x8_t qb[4];
-  {
-    const bf16x8_t zero = {};
-    const __bf16* qrow = a.q + ((int64_t)b * a.Hq + h_base + r) * kD;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qb[kk] = (r < gcnt) ? *(const bf16x8_t*)(qrow + dmap<DT>(kk, q4)) : zero;
-  }
+  const int32_t T = a.hdr[0], len = a.hdr[1], NP = a.hdr[2];
+  for (int32_t p = blockIdx.x; p < NP; p += gridDim.x) {
+    const int32_t pstart = p * len, pend = min(T, pstart + len);
+    for (int32_t b = a.first_seq[p]; b < a.batch; ++b) {
+      const int32_t cb = a.cum[b];
+      if (cb >= pend) break;
+      const int32_t L = clamp_len(a.seq_lens[b], cap);
+      const int32_t t_begin = max(pstart, cb) - cb;      // multiple of 32
+      const int32_t t_end = min(pend - cb, L);
+      if (t_begin >= t_end) continue;                    // only padding of b
+      const int32_t first_piece = cb / len;
+      const int32_t n_b = (cb + L - 1) / len - first_piece + 1;
+      const int32_t slot = p - first_piece;
 
-  const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
-  f32x4_t o[8];
+      // segment prologue: table slice and Q, issued together
+      const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+      const int32_t ib0 = t_begin >> a.bs_log2;
+      const int32_t nent = ((t_end - 1) >> a.bs_log2) - ib0 + 1;   // <= kTabCap
+      const int32_t tb0 = (int32_t)threadIdx.x < nent ? trow[ib0 + threadIdx.x] : 0;
+      const int32_t tb1 = (int32_t)threadIdx.x + 256 < nent ? trow[ib0 + threadIdx.x + 256] : 0;
+      bf16x8_t qb[4];
+      {
+        const bf16x8_t zero = {};
+        const __bf16* qrow = a.q + ((int64_t)b * a.Hq + h_base + r) * kD;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+        for (int kk = 0; kk < 4; ++kk)
+          qb[kk] = (r < gcnt) ? *(const bf16x8_t*)(qrow + dmap<DT>(kk, q4)) : zero;
+      }
+      __syncthreads();                   // previous segment's LDS readers are done
+      if ((int32_t)threadIdx.x < nent) s_tab[threadIdx.x] = clamp_block(tb0, a.num_blocks);
+      if ((int32_t)threadIdx.x + 256 < nent) s_tab[threadIdx.x + 256] = clamp_block(tb1, a.num_blocks);
+      __syncthreads();
 
-  const int32_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-  for (int32_t it = wave; it < n_tiles; it += kWaves) {
-    const int32_t t0 = t_begin + it * kTile;
-    const bool partial = t0 + kTile > t_end;
-
-    // ---- K: A operand rows = tokens t0 + 8*(r/4) + 4*s + r%4 (subtile s)
-    bf16x8_t ka[2][4];
+      WaveState st;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int32_t tok = min(t0 + 8 * (r >> 2) + 4 * s + (r & 3), t_end - 1);
-      load_k<LAYOUT, DT>(a, trow, hkv, tok, q4, ka[s]);
-    }
+      for (int n = 0; n < 8; ++n) st.o[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      st.m = kNegInf;
+      st.l = 0.f;
 
-    // ---- V: NHD rows go through LDS; preshuffled V is loaded as V^T directly
-    bf16x8_t va[8];
-    if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-      const int a4 = lane >> 4, c16 = lane & 15;
+      // Tiles of this wave: wave, wave + 4, ...  Two register buffers: the
+      // next tile's loads are in flight while the current tile is consumed
+      // (the scheduling barriers keep the compiler from sinking them).
+      const int32_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+      TileRaw A, B;
+      issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + wave * kTile, t_end, lane, A);
+      for (int32_t it = wave; it < n_tiles; it += 2 * kWaves) {
+        issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + (it + kWaves) * kTile, t_end, lane, B);
+        __builtin_amdgcn_sched_barrier(0);
+        consume_tile<LAYOUT, DT>(a, A, qb, t_begin + it * kTile, t_end, lane, vt, st);
+        if (it + kWaves >= n_tiles) break;
+        issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + (it + 2 * kWaves) * kTile, t_end, lane, A);
+        __builtin_amdgcn_sched_barrier(0);
+        consume_tile<LAYOUT, DT>(a, B, qb, t_begin + (it + kWaves) * kTile, t_end, lane, vt, st);
+      }
+
+      // ---- merge the 4 waves
+      float l_run = st.l;
+      l_run += __shfl_xor(l_run, 16);
+      l_run += __shfl_xor(l_run, 32);
+      if (q4 == 0) {
+        sm_m[wave][r] = st.m;
+        sm_l[wave][r] = l_run;
+      }
+      __syncthreads();
+      float M = kNegInf;
 #pragma unroll
-      for (int j4 = 0; j4 < 8; ++j4) {
-        const int j = 4 * j4 + a4;
-        const int32_t tok = min(t0 + j, t_end - 1);
-        const int32_t blk = clamp_block(trow[tok >> a.bs_log2], a.num_blocks);
-        const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
-        u32x4_t w;
-        if constexpr (DT == KV_DTYPE_BF16) {
-          w = *(const u32x4_t*)(a.vc + row * (kD * 2) + c16 * 16);
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
+      float Lt = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][r];
+        Lt += (mw == kNegInf) ? 0.f : sm_l[w][r] * fast_exp2(mw - M);
+      }
+      const float f = (st.m == kNegInf || !(Lt > 0.f)) ? 0.f : fast_exp2(st.m - M) / Lt;
+      float* ob = (float*)vt;            // [16 heads][128 dims] fp32
+#pragma unroll
+      for (int n = 0; n < 8; ++n) *(f32x4_t*)(ob + r * kD + 16 * n + 4 * q4) = st.o[n] * f;
+      __syncthreads();
+
+      const bool final_out = (n_b == 1);
+      for (int idx = threadIdx.x; idx < gcnt * (kD / 4); idx += 256) {
+        const int g = idx / (kD / 4), d4 = idx - g * (kD / 4);
+        f32x4_t s4 = *(const f32x4_t*)((const float*)smem + g * kD + 4 * d4);
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+          s4 += *(const f32x4_t*)((const float*)(smem + w * kVTileBytes) + g * kD + 4 * d4);
+        s4 *= a.v_scale;
+        const int64_t bh = (int64_t)b * a.Hq + h_base + g;
+        if (final_out) {
+          const bf16x4_t v4 = {(__bf16)s4[0], (__bf16)s4[1], (__bf16)s4[2], (__bf16)s4[3]};
+          *(bf16x4_t*)(a.out + bh * kD + 4 * d4) = v4;
         } else {
-          const u32x2_t c = *(const u32x2_t*)(a.vc + row * kD + c16 * 8);
-          w = __builtin_bit_cast(u32x4_t, fp8x8_to_bf16(c));
+          *(f32x4_t*)(a.part_o + (bh * a.n_slots + slot) * kD + 4 * d4) = s4;
         }
-        *(u32x4_t*)(vt + j * kVRowBytes + c16 * 16) = w;
       }
-    } else {
-      constexpr int X = (DT == KV_DTYPE_BF16) ? 8 : 16;
-      const int32_t tv = t0 + 8 * q4;                        // 8 tokens, aligned to 8
-      const int32_t tb = min(tv, (t_end - 1) & ~7);
-      const int32_t blk = clamp_block(trow[tb >> a.bs_log2], a.num_blocks);
-      const int32_t off = tb & (a.bs - 1);
-      const int64_t base = (((int64_t)blk * a.Hkv + hkv) * (a.bs / X) + off / X) * kD;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int64_t e = (base + 16 * n + r) * X + (off % X);
-        if constexpr (DT == KV_DTYPE_BF16) va[n] = *(const bf16x8_t*)(a.vc + e * 2);
-        else va[n] = fp8x8_to_bf16(*(const u32x2_t*)(a.vc + e));
+      if ((int)threadIdx.x < gcnt) {
+        const int g = threadIdx.x;
+        float Mg = kNegInf;
+        for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, sm_m[w][g]);
+        float Lg = 0.f;
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = sm_m[w][g];
+          Lg += (mw == kNegInf) ? 0.f : sm_l[w][g] * fast_exp2(mw - Mg);
+        }
+        const float lse_v = (Mg + __log2f(Lg)) * kLn2;
+        const int64_t bh = (int64_t)b * a.Hq + h_base + g;
+        if (final_out) {
+          if (a.lse) a.lse[bh] = lse_v;
+        } else {
+          a.part_lse[bh * a.n_slots + slot] = lse_v;
+        }
       }
-      if (partial) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (tv + jj >= t_end) {
-#pragma unroll
-            for (int n = 0; n < 8; ++n) va[n][jj] = (__bf16)0.f;
-          }
-      }
-    }
-
-    // ---- S^T = K Q^T: element i of acc[s] is token t0 + 8*q4 + 4*s + i, head r
-    f32x4_t acc[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc[s] = mfma16(ka[s][kk], qb[kk], acc[s]);
-    }
-    float sc[8];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t tok = t0 + 8 * q4 + 4 * s + i;
-        sc[4 * s + i] = (partial && tok >= t_end) ? kNegInf : acc[s][i] * a.qk_mult;
-      }
-
-    // ---- online softmax for query head r (exp2 domain)
-    float mt = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);    // finite: every tile has a valid token
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(sc[i] - m_new);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;            // lane-partial; reduced at the end
-    m_run = m_new;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) o[n] *= alpha;
-    const bf16x8_t pb = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3],
-                         (__bf16)p[4], (__bf16)p[5], (__bf16)p[6], (__bf16)p[7]};
-
-    // ---- O^T += V^T P^T: element i of o[n] is dim 16n + 4*q4 + i, head r
-    if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-      order_lds();
-      const int row0 = 8 * q4 + (r >> 2);
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int colb = (16 * n + 4 * (r & 3)) * 2;
-        const s16x4_t lo = lds_read_tr16(vt + row0 * kVRowBytes + colb);
-        const s16x4_t hi = lds_read_tr16(vt + (row0 + 4) * kVRowBytes + colb);
-        o[n] = mfma16(cat_tr(lo, hi), pb, o[n]);
-      }
-      order_lds();
-    } else {
-#pragma unroll
-      for (int n = 0; n < 8; ++n) o[n] = mfma16(va[n], pb, o[n]);
-    }
-  }
-
-  // ---- merge the 4 waves
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (q4 == 0) {
-    sm_m[wave][r] = m_run;
-    sm_l[wave][r] = l_run;
-  }
-  __syncthreads();
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
-  float Lt = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm_m[w][r];
-    Lt += (mw == kNegInf) ? 0.f : sm_l[w][r] * fast_exp2(mw - M);
-  }
-  const float f = (m_run == kNegInf || !(Lt > 0.f)) ? 0.f : fast_exp2(m_run - M) / Lt;
-  float* ob = (float*)vt;                    // [16 heads][128 dims] fp32
-#pragma unroll
-  for (int n = 0; n < 8; ++n) *(f32x4_t*)(ob + r * kD + 16 * n + 4 * q4) = o[n] * f;
-  __syncthreads();
-
-  const bool final_out = (n_b == 1);
-  for (int idx = threadIdx.x; idx < gcnt * (kD / 4); idx += 256) {
-    const int g = idx / (kD / 4), d4 = idx - g * (kD / 4);
-    f32x4_t s4 = *(const f32x4_t*)((const float*)smem + g * kD + 4 * d4);
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-      s4 += *(const f32x4_t*)((const float*)(smem + w * kVTileBytes) + g * kD + 4 * d4);
-    s4 *= a.v_scale;
-    const int64_t bh = (int64_t)b * a.Hq + h_base + g;
-    if (final_out) {
-      const bf16x4_t v4 = {(__bf16)s4[0], (__bf16)s4[1], (__bf16)s4[2], (__bf16)s4[3]};
-      *(bf16x4_t*)(a.out + bh * kD + 4 * d4) = v4;
-    } else {
-      *(f32x4_t*)(a.part_o + (bh * a.n_splits + split) * kD + 4 * d4) = s4;
-    }
-  }
-  if (threadIdx.x < gcnt) {
-    const int g = threadIdx.x;
-    float Mg = kNegInf;
-    for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, sm_m[w][g]);
-    float Lg = 0.f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][g];
-      Lg += (mw == kNegInf) ? 0.f : sm_l[w][g] * fast_exp2(mw - Mg);
-    }
-    const float lse_v = (Mg + __log2f(Lg)) * kLn2;
-    const int64_t bh = (int64_t)b * a.Hq + h_base + g;
-    if (final_out) {
-      if (a.lse) a.lse[bh] = lse_v;
-    } else {
-      a.part_lse[bh * a.n_splits + split] = lse_v;
     }
   }
 }
 
 // Second pass: o = sum_i w_i o_i / sum_i w_i with w_i = exp(lse_i - max lse),
-// lse = max + ln sum_i w_i.  One wave per (request, query head).
+// lse = max + ln sum_i w_i, over the pieces of each request that spans more
+// than one piece.  One wave per (request, query head).
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
   if (bh >= (int64_t)a.batch * a.Hq) return;
   const int32_t b = (int32_t)(bh / a.Hq);
-  int32_t L = a.seq_lens[b];
-  const int32_t cap = a.max_blocks << a.bs_log2;
-  L = L > cap ? cap : L;
-  const int32_t n_b = (L + a.split_tokens - 1) / a.split_tokens;
-  if (n_b <= 1) return;                      // written by the first pass
-  const float* pl = a.part_lse + bh * a.n_splits;
+  const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
+  if (L == 0) return;
+  const int32_t len = a.hdr[1];
+  const int32_t cb = a.cum[b];
+  const int32_t n_b = (cb + L - 1) / len - cb / len + 1;
+  if (n_b <= 1) return;                      // written by the main pass
+  const float* pl = a.part_lse + bh * a.n_slots;
   float M = kNegInf;
   for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i]);
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
-  const f32x2_t* po = (const f32x2_t*)(a.part_o + bh * a.n_splits * kD) + lane;
+  const f32x2_t* po = (const f32x2_t*)(a.part_o + bh * a.n_slots * kD) + lane;
   for (int i = 0; i < n_b; ++i) {
     const float w = fast_exp2((pl[i] - M) * kLog2e);
     wsum += w;
@@ -357,23 +511,45 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
+static int32_t log2_ceil(int32_t v) {
+  int32_t l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+static int32_t device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t split_tokens) {
   DecodePlan p;
   const int32_t G = num_q_heads / c.num_kv_heads;
   p.n_gchunks = (G + 15) / 16;
-  if (split_tokens <= 0) {
-    // Largest split (<= 1024 tokens) that still gives ~32 workgroups per CU
-    // for the longest request; short batches fall back to 128-token splits.
-    const int64_t units = (int64_t)batch * c.num_kv_heads * p.n_gchunks;
-    split_tokens = 1024;
-    while (split_tokens > 128 &&
-           units * ((max_seq_len + split_tokens - 1) / split_tokens) < 8192)
-      split_tokens >>= 1;
+  const int32_t groups = c.num_kv_heads * p.n_gchunks;
+  // a piece's block ids must fit the LDS table: len/bs + 1 <= kTabCap
+  int64_t len_max = ((int64_t)(kTabCap - 1) << log2_ceil(c.block_size)) & ~(int64_t)31;
+  if (len_max > 16384) len_max = 16384;
+  p.len_max = (int32_t)len_max;
+  if (split_tokens > 0) {
+    p.fixed_len = split_tokens < p.len_max ? split_tokens : p.len_max;
+    p.len_min = p.fixed_len;
+  } else {
+    p.fixed_len = 0;
+    p.len_min = 256 < p.len_max ? 256 : p.len_max;
   }
-  p.split_tokens = split_tokens;
-  p.n_splits = (max_seq_len + split_tokens - 1) / split_tokens;
-  if (p.n_splits < 1) p.n_splits = 1;
+  // grid: two rounds of two resident workgroups per CU, shared by the groups
+  const int32_t slots = device_cu_count() * 2 * 2;
+  p.pieces_per_group = slots / groups > 0 ? slots / groups : 1;
+  p.split_tokens = p.fixed_len;
+  p.n_slots = (max_seq_len + p.len_min - 1) / p.len_min + 1;
+  const int64_t padded = (int64_t)batch * ((max_seq_len + 31) & ~31);
+  p.max_pieces = (int32_t)((padded + p.len_min - 1) / p.len_min) + 1;
+  p.n_splits = p.n_slots;
   return p;
 }
 
@@ -381,14 +557,15 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_heads,
                               int32_t head_dim) {
-  const size_t rows = (size_t)batch * num_q_heads * p.n_splits;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+  const size_t rows = (size_t)batch * num_q_heads * p.n_slots;
+  return 256 + align256((size_t)(batch + 1) * 4) + align256((size_t)p.max_pieces * 4) +
+         align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
 
 hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
                          int32_t batch, int32_t num_q_heads, const int32_t* tables,
-                         int32_t max_blocks, const int32_t* seq_lens, float scale,
-                         void* out, float* lse, void* workspace, hipStream_t s) {
+                         int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, void* out, float* lse, void* workspace, hipStream_t s) {
   DecodeArgs a;
   a.kc = (const uint8_t*)c.k_cache;
   a.vc = (const uint8_t*)c.v_cache;
@@ -397,26 +574,41 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   a.seq_lens = seq_lens;
   a.out = (__bf16*)out;
   a.lse = lse;
-  const size_t rows = (size_t)batch * num_q_heads * p.n_splits;
-  a.part_o = (float*)workspace;
-  a.part_lse = (float*)((uint8_t*)workspace + align256(rows * c.head_dim * sizeof(float)));
+  uint8_t* w = (uint8_t*)workspace;
+  a.hdr = (int32_t*)w;
+  w += 256;
+  a.cum = (int32_t*)w;
+  w += align256((size_t)(batch + 1) * 4);
+  a.first_seq = (int32_t*)w;
+  w += align256((size_t)p.max_pieces * 4);
+  const size_t rows = (size_t)batch * num_q_heads * p.n_slots;
+  a.part_o = (float*)w;
+  w += align256(rows * c.head_dim * sizeof(float));
+  a.part_lse = (float*)w;
   a.max_blocks = max_blocks;
   a.num_blocks = c.num_blocks;
   a.bs = c.block_size;
-  a.bs_log2 = 0;
-  while ((1 << a.bs_log2) < c.block_size) ++a.bs_log2;
+  a.bs_log2 = log2_ceil(c.block_size);
+  const int64_t capacity = (int64_t)max_blocks << a.bs_log2;
+  a.max_len = (int32_t)(capacity < max_seq_len ? capacity : max_seq_len);
   a.Hkv = c.num_kv_heads;
   a.Hq = num_q_heads;
   a.G = num_q_heads / c.num_kv_heads;
   a.n_gchunks = p.n_gchunks;
-  a.split_tokens = p.split_tokens;
-  a.n_splits = p.n_splits;
+  a.n_slots = p.n_slots;
   a.batch = batch;
+  a.fixed_len = p.fixed_len;
+  a.len_min = p.len_min;
+  a.len_max = p.len_max;
+  a.target_pieces = p.pieces_per_group;
   a.qk_mult = scale * c.k_scale * kLog2e;
   a.v_scale = c.v_scale;
-  dim3 grid((unsigned)p.n_splits, (unsigned)(c.num_kv_heads * p.n_gchunks), (unsigned)batch);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)p.pieces_per_group, (unsigned)(c.num_kv_heads * p.n_gchunks));
 #define PKV_LAUNCH(L, T) \
-  hipLaunchKernelGGL((decode_split_kernel<L, T>), grid, dim3(256), 0, s, a)
+  hipLaunchKernelGGL((decode_piece_kernel<L, T>), grid, dim3(256), 0, s, a)
   if (c.layout == KV_LAYOUT_NHD) {
     if (c.dtype == KV_DTYPE_BF16) PKV_LAUNCH(KV_LAYOUT_NHD, KV_DTYPE_BF16);
     else PKV_LAUNCH(KV_LAYOUT_NHD, KV_DTYPE_FP8_E4M3);
@@ -425,14 +617,11 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
     else PKV_LAUNCH(KV_LAYOUT_PRESHUFFLED, KV_DTYPE_FP8_E4M3);
   }
 #undef PKV_LAUNCH
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.n_splits > 1) {
-    const int64_t bh = (int64_t)batch * num_q_heads;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((bh + 3) / 4)), dim3(256), 0, s, a);
-    e = hipGetLastError();
-  }
-  return e;
+  const int64_t bh = (int64_t)batch * num_q_heads;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((bh + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

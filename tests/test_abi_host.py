@@ -106,21 +106,26 @@ def test_decode_argument_errors():
     assert call(mb=8) == pk.KV_EINVAL                 # 8 blocks * 16 < 512 tokens
     assert call(q=None) == pk.KV_EINVAL
     assert call(out=FAKE + 4) == pk.KV_EINVAL
-    assert call(split=100) == pk.KV_EINVAL            # not a multiple of 128
-    assert call(split=128, wsb=16) == pk.KV_ENOSPC    # 4 splits need a workspace
-    assert call(split=128, ws=None) == pk.KV_EINVAL
+    assert call(split=100) == pk.KV_EINVAL            # not a multiple of 32
+    assert call(split=128, wsb=16) == pk.KV_ENOSPC    # the plan needs a workspace
+    assert call(ws=None) == pk.KV_EINVAL
 
 
 def test_decode_workspace_closed_form():
+    """header + prefix sums + piece list + fp32 partial slots (o then lse)."""
     c = _cache(num_kv_heads=8)
     L = pk.lib()
     B, Hq, msl = 64, 64, 8192
+    a256 = lambda x: -(-x // 256) * 256
     for split in (128, 512, 1024):
-        n_splits = -(-msl // split)
-        rows = B * Hq * n_splits
-        want = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+        n_slots = -(-msl // split) + 1
+        max_pieces = -(-(B * msl) // split) + 1
+        rows = B * Hq * n_slots
+        want = 256 + a256(4 * (B + 1)) + a256(4 * max_pieces) + a256(rows * 128 * 4) + a256(rows * 4)
         assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, Hq, msl, split) == want
     assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, 63, msl, 0) == 0   # invalid -> 0
+    # batch * max_seq_len at 2^31 is rejected
+    assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), 65535, Hq, 1 << 16, 0) == 0
 
 
 def test_pack_sizes_and_errors():
