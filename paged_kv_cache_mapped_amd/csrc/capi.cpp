@@ -203,7 +203,8 @@ size_t extend_attn_workspace_bytes(const kv_cache_t* cache, int32_t num_seqs, in
   if (extend_checks(cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget,
                     "extend_attn_workspace_bytes"))
     return 0;
-  const pkv::ExtendPlan p = pkv::plan_extend(*cache, num_seqs, max_ctx_len, budget);
+  const pkv::ExtendPlan p =
+      pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget);
   return pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
 }
 
@@ -226,7 +227,8 @@ int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return fail(KV_EINVAL, "%s: q, k_new, v_new and out must be 16-byte aligned", fn);
   if (num_q_heads > 65535 || num_seqs > 65535) return fail(KV_EINVAL, "%s: grid too large", fn);
-  const pkv::ExtendPlan p = pkv::plan_extend(*cache, num_seqs, max_ctx_len, budget);
+  const pkv::ExtendPlan p =
+      pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget);
   const size_t need = pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
   if (need > 0) {
     if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);

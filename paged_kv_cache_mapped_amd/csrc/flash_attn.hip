@@ -33,6 +33,8 @@
 // Keys are read either from contiguous [tokens, H_kv, D] tensors (prefill, and
 // the new tokens of an extend) or straight from the paged NHD cache through
 // the block table (extend context chunks) -- no gather copy.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -43,10 +45,10 @@ constexpr int kD = 128;
 constexpr int kBM = 128;                   // query rows per workgroup
 constexpr int kBN = 64;                    // keys per tile
 constexpr int kKRow = 272;                 // LDS bytes per K row (256 + 16 pad)
-constexpr int kVRow = 288;                 // LDS bytes per V row (256 + 32 pad)
+constexpr int kVRow = 320;                 // LDS bytes per V row (256 + 64 pad)
 constexpr int kKTile = kBN * kKRow;
 constexpr int kVTile = kBN * kVRow;
-constexpr int kStage = kKTile + kVTile;    // 35840 bytes
+constexpr int kStage = kKTile + kVTile;    // 37888 bytes
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct AttnArgs {
@@ -98,18 +100,44 @@ __device__ __forceinline__ int64_t key_row_bytes(const AttnArgs& a, const KeySrc
 
 // Each thread stages rows tid/16 + 16*j (j = 0..3), 16-byte chunk tid%16, of
 // the K and V tiles; keys past k_end are clamped to the last key (finite data
-// whose probability is exactly zero).
+// whose probability is exactly zero).  Contiguous keys: kth / vth point at the
+// thread's first row of the first tile and advance by a constant per tile;
+// paged keys look their blocks up in the table.
 template <bool PAGED>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const KeySrc& s, int32_t k0,
+__device__ __forceinline__ void load_tile(const AttnArgs& a, const KeySrc& s, const uint8_t* kth,
+                                          const uint8_t* vth, int32_t k0, int32_t k_begin,
                                           int32_t k_end, u32x4_t (&rk)[4], u32x4_t (&rv)[4]) {
   const int c = threadIdx.x & 15;
+  if constexpr (!PAGED) {
+    const int64_t row_stride = (int64_t)a.Hkv * (kD * 2);
+    const int64_t toff = (int64_t)(k0 - k_begin) * row_stride;
+    const uint8_t* kb = kth + toff;
+    const uint8_t* vb = vth + toff;
+    if (k0 + kBN <= k_end) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int32_t key = k0 + (threadIdx.x >> 4) + 16 * j;
-    key = key < k_end ? key : k_end - 1;
-    const int64_t off = key_row_bytes<PAGED>(a, s, key) + c * 16;
-    rk[j] = *(const u32x4_t*)(s.kb + off);
-    rv[j] = *(const u32x4_t*)(s.vb + off);
+      for (int j = 0; j < 4; ++j) {
+        rk[j] = *(const u32x4_t*)(kb + 16 * j * row_stride);
+        rv[j] = *(const u32x4_t*)(vb + 16 * j * row_stride);
+      }
+    } else {
+      const int32_t r0 = k0 + (threadIdx.x >> 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int32_t key = r0 + 16 * j;
+        const int64_t d = (int64_t)((key < k_end ? key : k_end - 1) - r0) * row_stride;
+        rk[j] = *(const u32x4_t*)(kb + d);
+        rv[j] = *(const u32x4_t*)(vb + d);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int32_t key = k0 + (threadIdx.x >> 4) + 16 * j;
+      key = key < k_end ? key : k_end - 1;
+      const int64_t off = key_row_bytes<PAGED>(a, s, key) + c * 16;
+      rk[j] = *(const u32x4_t*)(s.kb + off);
+      rv[j] = *(const u32x4_t*)(s.vb + off);
+    }
   }
 }
 
@@ -124,35 +152,47 @@ __device__ __forceinline__ void store_tile(uint8_t* stage, const u32x4_t (&rk)[4
   }
 }
 
-// Attention of 128 query rows (rows q0.. of a sequence whose row 0 is global
-// row qbase) of head h against keys [k_begin, k_end).  CAUSAL: key j is visible
-// to row i iff j <= i.  Writes bf16 output + lse, or an fp32 partial.
-template <bool PAGED, bool CAUSAL, bool PARTIAL>
-__device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, int32_t h,
-                           int64_t qbase, int32_t q0, int32_t qn, int32_t k_begin, int32_t k_end,
-                           int32_t part) {
+// Per-wave state of a 128-row query block: Q^T (B operand), O^T accumulators
+// and the running exp2-domain max / lane-partial sum of each lane's row.
+struct RowState {
+  bf16x8_t qb[8];
+  f32x16_t o[4];
+  float m_run, l_run;
+};
+
+// Load Q (rows q0.. of a sequence whose row 0 is global row qbase) and clear
+// the running state.
+__device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t qbase, int32_t q0,
+                                          int32_t qn, RowState& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, hh = lane >> 5;
+  const int32_t row = q0 + 32 * wave + r;
+  // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
+  const bf16x8_t zero = {};
+  const __bf16* qp = a.q + ((qbase + row) * a.Hq + h) * kD + 8 * hh;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) S.qb[ks] = row < qn ? *(const bf16x8_t*)(qp + 16 * ks) : zero;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S.o[dt][i] = 0.f;
+  S.m_run = kNegInf;
+  S.l_run = 0.f;
+}
+
+// Fold keys [k_begin, k_end) of one source into the running state.  CAUSAL:
+// key j is visible to row i iff j <= i (keys and rows indexed within the
+// sequence).  The LDS double buffer is filled and drained inside, so phases
+// with different sources can follow each other.
+template <bool PAGED, bool CAUSAL, bool FIRST = false>
+__device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
+                                         int32_t q0, int32_t qn, int32_t k_begin, int32_t k_end,
+                                         RowState& S) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
   const int32_t row = q0 + 32 * wave + r;       // this lane's query row (in sequence)
-  const int32_t wrow0 = q0 + 32 * wave;         // first row of this wave
-
-  // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
-  bf16x8_t qb[8];
-  {
-    const bf16x8_t zero = {};
-    const __bf16* qp = a.q + ((qbase + row) * a.Hq + h) * kD + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qb[ks] = row < qn ? *(const bf16x8_t*)(qp + 16 * ks) : zero;
-  }
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
 
   // key range actually needed by this block
   int32_t kend = k_end;
@@ -160,19 +200,28 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
     const int32_t last_row = min(q0 + kBM, qn) - 1;
     kend = min(kend, last_row + 1);
   }
-  if (kend <= k_begin) return;               // never taken: callers pass a non-empty range
+  if (kend <= k_begin) return;               // uniform over the workgroup
   const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
 
+  const int64_t th_off = ((int64_t)(k_begin + (threadIdx.x >> 4)) * a.Hkv + src.hkv) * (kD * 2) +
+                         (threadIdx.x & 15) * 16;
+  const uint8_t* kth = src.kb + th_off;       // contiguous keys only
+  const uint8_t* vth = src.vb + th_off;
   u32x4_t rk[4], rv[4];
-  load_tile<PAGED>(a, src, k_begin, kend, rk, rv);
+  if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
+  load_tile<PAGED>(a, src, kth, vth, k_begin, k_begin, kend, rk, rv);
   store_tile(smem, rk, rv);
   __syncthreads();
 
-  for (int32_t t = 0; t < n_tiles; ++t) {
+  // One key tile.  MASK = false for tiles that no row of the workgroup needs
+  // masked (the whole tile is inside the key range and, for causal blocks,
+  // below the diagonal of the first row); the mask code is not emitted there.
+  auto step = [&](int32_t t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int32_t k0 = k_begin + t * kBN;
     uint8_t* st = smem + (t & 1) * kStage;
     const bool more = t + 1 < n_tiles;
-    if (more) load_tile<PAGED>(a, src, k0 + kBN, kend, rk, rv);
+    if (more) load_tile<PAGED>(a, src, kth, vth, k0 + kBN, k_begin, kend, rk, rv);
 
     // ---- S^T = K Q^T
     f32x16_t s[2];
@@ -182,17 +231,11 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
       for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
       const uint8_t* kp = st + (32 * ks2 + r) * kKRow + 16 * hh;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[ks2] = mfma32(*(const bf16x8_t*)(kp + 32 * ks), qb[ks], s[ks2]);
+      for (int ks = 0; ks < 8; ++ks) s[ks2] = mfma32(*(const bf16x8_t*)(kp + 32 * ks), S.qb[ks], s[ks2]);
     }
 
-    // ---- scale, mask, online softmax (row = this lane's query row)
-    bool need_mask = k0 + kBN > kend;
-    if constexpr (CAUSAL) need_mask = need_mask || (k0 + kBN - 1 > wrow0);
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[ks2][i] *= a.qk_mult;
-    if (need_mask) {
+    // ---- mask, online softmax on raw scores (row = this lane's query row)
+    if constexpr (MASK) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
@@ -208,22 +251,28 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.qk_mult;     // exp2 domain
+    // Lazy rescale: the reference max only moves when some row's max grew by
+    // more than 8, so probabilities stay <= 2^8 and most tiles skip the O^T
+    // rescale.  Any reference works: numerator and denominator share it.
+    if (__builtin_amdgcn_ballot_w64(mt > S.m_run + 8.f) != 0) {
+      const float m_new = fmaxf(S.m_run, mt);
+      const float alpha = fast_exp2(S.m_run - (m_new == kNegInf ? 0.f : m_new));
+      S.l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) S.o[dt] *= alpha;
+      S.m_run = m_new;
+    }
+    const float m_use = (S.m_run == kNegInf) ? 0.f : S.m_run;
     float psum = 0.f;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[ks2][i] = fast_exp2(s[ks2][i] - m_use);
+        s[ks2][i] = fast_exp2(__builtin_fmaf(s[ks2][i], a.qk_mult, -m_use));
         psum += s[ks2][i];
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    S.l_run += psum;
 
     // P^T as B operand: k-step kk covers keys 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}
     bf16x8_t pb[4];
@@ -242,19 +291,37 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
         const int colb = (32 * dt + 16 * (g16 & 1) + 4 * (l16 & 3)) * 2;
         const s16x4_t lo = lds_read_tr16(vt + vrow * kVRow + colb);
         const s16x4_t hi = lds_read_tr16(vt + (vrow + 8) * kVRow + colb);
-        o[dt] = mfma32(cat_tr(lo, hi), pb[kk], o[dt]);
+        S.o[dt] = mfma32(cat_tr(lo, hi), pb[kk], S.o[dt]);
       }
     }
 
     if (more) store_tile(smem + ((t + 1) & 1) * kStage, rk, rv);
     __syncthreads();
-  }
+  };
 
-  // ---- epilogue
-  l_run += __shfl_xor(l_run, 32);
+  int32_t t_plain = (kend - k_begin) / kBN;             // tiles fully inside the key range
+  if constexpr (CAUSAL) {
+    const int32_t c = q0 - k_begin - (kBN - 1);          // last key of tile <= first row
+    const int32_t tc = c >= 0 ? c / kBN + 1 : 0;
+    t_plain = t_plain < tc ? t_plain : tc;
+  }
+  int32_t t = 0;
+  for (; t < t_plain; ++t) step(t, std::false_type{});
+  for (; t < n_tiles; ++t) step(t, std::true_type{});
+}
+
+// Write the rows of this block: bf16 output + lse, or an fp32 partial
+// (normalised o and its lse) of part `part`.
+template <bool PARTIAL>
+__device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_t qbase,
+                                            int32_t q0, int32_t qn, int32_t part, RowState& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, hh = lane >> 5;
+  const int32_t row = q0 + 32 * wave + r;
+  const float l_run = S.l_run + __shfl_xor(S.l_run, 32);
   if (row >= qn) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  const float lse_v = l_run > 0.f ? (S.m_run + __log2f(l_run)) * kLn2 : kNegInf;
   const int64_t grow = qbase + row;
   if constexpr (PARTIAL) {
     float* op = a.part_o + (((int64_t)part * a.rows + grow) * a.Hq + h) * kD;
@@ -262,8 +329,8 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4_t v4 = {o[dt][4 * i4] * inv, o[dt][4 * i4 + 1] * inv, o[dt][4 * i4 + 2] * inv,
-                            o[dt][4 * i4 + 3] * inv};
+        const f32x4_t v4 = {S.o[dt][4 * i4] * inv, S.o[dt][4 * i4 + 1] * inv,
+                            S.o[dt][4 * i4 + 2] * inv, S.o[dt][4 * i4 + 3] * inv};
         *(f32x4_t*)(op + 32 * dt + 8 * i4 + 4 * hh) = v4;
       }
     if (hh == 0) a.part_lse[((int64_t)part * a.rows + grow) * a.Hq + h] = lse_v;
@@ -273,12 +340,37 @@ __device__ void attn_block(const AttnArgs& a, uint8_t* smem, const KeySrc& src, 
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const bf16x4_t v4 = {(__bf16)(o[dt][4 * i4] * inv), (__bf16)(o[dt][4 * i4 + 1] * inv),
-                             (__bf16)(o[dt][4 * i4 + 2] * inv), (__bf16)(o[dt][4 * i4 + 3] * inv)};
+        const bf16x4_t v4 = {(__bf16)(S.o[dt][4 * i4] * inv), (__bf16)(S.o[dt][4 * i4 + 1] * inv),
+                             (__bf16)(S.o[dt][4 * i4 + 2] * inv), (__bf16)(S.o[dt][4 * i4 + 3] * inv)};
         *(bf16x4_t*)(op + 32 * dt + 8 * i4 + 4 * hh) = v4;
       }
     if (hh == 0 && a.lse) a.lse[grow * a.Hq + h] = lse_v;
   }
+}
+
+__device__ __forceinline__ KeySrc contiguous_keys(const AttnArgs& a, int32_t s0, int32_t hkv) {
+  KeySrc src;
+  src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
+  src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
+  src.trow = nullptr;
+  src.hkv = hkv;
+  return src;
+}
+
+__device__ __forceinline__ KeySrc paged_keys(const AttnArgs& a, int32_t seq, int32_t hkv) {
+  KeySrc src;
+  src.kb = a.kc;
+  src.vb = a.vc;
+  src.trow = a.tables + (int64_t)seq * a.max_blocks;
+  src.hkv = hkv;
+  return src;
+}
+
+__device__ __forceinline__ int32_t context_len(const AttnArgs& a, int32_t seq) {
+  int32_t C = a.ctx_lens[seq];
+  const int32_t cap = a.max_blocks << a.bs_log2;
+  C = C > cap ? cap : C;
+  return C < 0 ? 0 : C;
 }
 
 // Logical order: (seq, kv head, query head in group, query tile descending),
@@ -299,17 +391,18 @@ void prefill_kernel(AttnArgs a) {
   const int32_t qn = a.cu[seq + 1] - s0;
   const int32_t q0 = qt * kBM;
   if (q0 >= qn) return;
-  KeySrc src;
-  src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
-  src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
-  src.trow = nullptr;
-  src.hkv = hkv;
-  attn_block<false, CAUSAL, false>(a, smem, src, hkv * a.G + g, s0, q0, qn, 0, qn, 0);
+  const int32_t h = hkv * a.G + g;
+  RowState S;
+  init_rows(a, h, s0, q0, qn, S);
+  run_keys<false, CAUSAL, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
+  finish_rows<false>(a, h, s0, q0, qn, 0, S);
 }
 
-// Logical order: (seq, part, kv head, query head, query tile descending).
-// Part 0: the new tokens among themselves (causal).  Part p >= 1: the new
-// tokens against context chunk p-1 = cached tokens [(p-1)*chunk, p*chunk).
+// Split extend.  Logical order: (seq, part, kv head, query head, query tile
+// descending).  Part 0: the new tokens among themselves (causal).  Part
+// p >= 1: the new tokens against context chunk p-1 = cached tokens
+// [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
+// fp32 partial; extend_merge_kernel combines them.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
@@ -328,27 +421,52 @@ void extend_kernel(AttnArgs a) {
   const int32_t q0 = qt * kBM;
   if (q0 >= qn) return;
   const int32_t h = hkv * a.G + g;
+  RowState S;
   if (part == 0) {
-    KeySrc src;
-    src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
-    src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
-    src.trow = nullptr;
-    src.hkv = hkv;
-    attn_block<false, true, true>(a, smem, src, h, s0, q0, qn, 0, qn, 0);
+    init_rows(a, h, s0, q0, qn, S);
+    run_keys<false, true, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
   } else {
-    int32_t C = a.ctx_lens[seq];
-    const int32_t cap = a.max_blocks << a.bs_log2;
-    C = C > cap ? cap : C;
+    const int32_t C = context_len(a, seq);
     const int32_t kb = (part - 1) * a.chunk_tokens;
     if (kb >= C) return;
-    const int32_t ke = min(C, kb + a.chunk_tokens);
-    KeySrc src;
-    src.kb = a.kc;
-    src.vb = a.vc;
-    src.trow = a.tables + (int64_t)seq * a.max_blocks;
-    src.hkv = hkv;
-    attn_block<true, false, true>(a, smem, src, h, s0, q0, qn, kb, ke, part);
+    init_rows(a, h, s0, q0, qn, S);
+    run_keys<true, false, true>(a, smem, paged_keys(a, seq, hkv), q0, qn, kb,
+                                min(C, kb + a.chunk_tokens), S);
   }
+  finish_rows<true>(a, h, s0, q0, qn, part, S);
+}
+
+// Fused extend, used when the batch has enough query tiles to fill the GPU
+// without splitting along the context.  Logical order: (seq, kv head, query
+// head, query tile descending).  One workgroup runs every context chunk of
+// its rows in order and then the new tokens, carrying one running softmax
+// state: the LSE merge of each chunk into the running output is done in
+// registers (rescaling by the exponential of the max difference), so no
+// partials are written and no merge pass is needed.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void extend_fused_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  const int64_t item = logical_item(a);
+  if (item >= a.items) return;
+  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
+  int64_t rest = item / a.n_qtiles;
+  const int32_t g = (int32_t)(rest % a.G);
+  rest /= a.G;
+  const int32_t hkv = (int32_t)(rest % a.Hkv);
+  const int32_t seq = (int32_t)(rest / a.Hkv);
+  const int32_t s0 = a.cu[seq];
+  const int32_t qn = a.cu[seq + 1] - s0;
+  const int32_t q0 = qt * kBM;
+  if (q0 >= qn) return;
+  const int32_t h = hkv * a.G + g;
+  const int32_t C = context_len(a, seq);
+  RowState S;
+  init_rows(a, h, s0, q0, qn, S);
+  const KeySrc ctx = paged_keys(a, seq, hkv);
+  for (int32_t kb = 0; kb < C; kb += a.chunk_tokens)
+    run_keys<true, false>(a, smem, ctx, q0, qn, kb, min(C, kb + a.chunk_tokens), S);
+  run_keys<false, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
+  finish_rows<false>(a, h, s0, q0, qn, 0, S);
 }
 
 // Final merge of the extend parts of each (row, head), one wave each:
@@ -424,8 +542,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   return hipGetLastError();
 }
 
-ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t max_ctx_len,
-                       int32_t chunk_budget_tokens) {
+ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
+                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens) {
   ExtendPlan p;
   // Per-request share of the budget, rounded down to whole key tiles and
   // blocks (at least one).
@@ -437,6 +555,11 @@ ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t max_ctx_le
   p.chunk_tokens = (int32_t)share;
   p.n_chunks = max_ctx_len > 0 ? (int32_t)((max_ctx_len + share - 1) / share) : 0;
   p.n_parts = p.n_chunks + 1;
+  // Fused when the query tiles alone give every CU two rounds of its two
+  // resident workgroups; otherwise the context chunks become extra grid
+  // parallelism and a merge pass combines them.
+  const int64_t tiles = (int64_t)num_q_heads * ((total_new + kBM - 1) / kBM);
+  p.fused = (p.n_chunks == 0 || tiles >= (int64_t)4 * device_cu_count()) ? 1 : 0;
   return p;
 }
 
@@ -444,6 +567,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
                               int32_t head_dim) {
+  if (p.fused) return 0;
   const size_t rows = (size_t)p.n_parts * total_new * num_q_heads;
   return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -481,6 +605,13 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.chunk_tokens = p.chunk_tokens;
   a.rows = total_new;
   a.qk_mult = scale * kLog2e;
+  if (p.fused) {
+    a.items = (int64_t)num_seqs * num_q_heads * a.n_qtiles;
+    a.grid_pad = (a.items + 7) & ~(int64_t)7;
+    if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(extend_fused_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   a.items = (int64_t)num_seqs * p.n_parts * num_q_heads * a.n_qtiles;
   a.grid_pad = (a.items + 7) & ~(int64_t)7;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;

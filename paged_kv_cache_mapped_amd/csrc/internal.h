@@ -9,6 +9,15 @@
 
 namespace pkv {
 
+// Compute units of the current device (256 on MI355X); host query, no sync.
+inline int32_t device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 // ----------------------------------------------------------------- kv_write
 hipError_t launch_kv_write(const kv_cache_t& c, const void* k, const void* v,
                            const int64_t* slots, int32_t num_tokens, hipStream_t s);
@@ -47,9 +56,10 @@ struct ExtendPlan {
   int32_t chunk_tokens;   // cached tokens per chunk (multiple of block_size)
   int32_t n_chunks;       // context chunks of the longest context
   int32_t n_parts;        // n_chunks + 1 (the new-token part)
+  int32_t fused;          // 1: one workgroup runs every part of its rows (no partials)
 };
-ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t max_ctx_len,
-                       int32_t chunk_budget_tokens);
+ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
+                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens);
 size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
                               int32_t head_dim);
 hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,

@@ -517,14 +517,6 @@ static int32_t log2_ceil(int32_t v) {
   return l;
 }
 
-static int32_t device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t split_tokens) {
   DecodePlan p;
