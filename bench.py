@@ -20,7 +20,11 @@ over one batch of seeded synthetic input that is already resident in HBM:
       prefill_attn.  value = query tokens / step time (tokens/s).
 
 Roofline: the dominant call's algorithmic bytes (or flops) per launch divided
-by its average duration from HIP events recorded on the stream it runs on.
+by its average duration, from HIP events recorded around it in every timed
+step on the stream the library launches on.  traffic: HBM bytes per
+call from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by what the same
+counters read for the pack kernel (a plain copy of known size), read from the
+committed profile when it was taken on the current kernel sources, else null.
 cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -45,6 +49,43 @@ METRIC = "paged decode HBM GB/s (% of 8 TB/s); mixed-batch attention tokens/s"
 
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+# Sources each roofline kernel is compiled from; a counter profile counts only
+# while their hash matches the one recorded when the counters were taken.
+KERNEL_SOURCES = {
+    "paged_decode": ["paged_decode.hip", "common.h"],
+    "prefill_attn": ["flash_attn.hip", "common.h"],
+    "extend_attn": ["flash_attn.hip", "common.h"],
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_cache_mapped_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per call of `kernel` from the committed counter profile, or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- `"):
+            k, v = line[3:].split("`", 1)
+            fields[k] = v.split(":", 1)[1].strip().strip("`")
+    try:
+        if fields["source_sha256"] != source_hash(kernel):
+            return None
+        return float(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -291,25 +332,41 @@ def main():
             step()
         torch.cuda.synchronize()
         _log(f"timing {args.steps} steps of {name}")
+        # HIP events on the stream the library launches on, around the dominant
+        # call of every timed step (events between every pair of calls would add
+        # a marker packet each to the step)
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
+        for s in range(args.steps):
+            for c in calls:
+                if c.name == dominant:
+                    ev[s][0].record(stream)
+                    c.fn()
+                    ev[s][1].record(stream)
+                else:
+                    c.fn()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / max(args.steps, 1)
+        dom_ms = sum(a.elapsed_time(b) for a, b in ev) / max(len(ev), 1)
 
-        # per-call durations from HIP events on the stream the library launches on
-        stream = torch.cuda.current_stream()
+        # every call's own duration, from events around it, after the timed region
         per = {}
         for c in calls:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
-            for a, b in evs:
-                a.record(stream)
-                c.fn()
-                b.record(stream)
-            torch.cuda.synchronize()
-            avg = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+            if c.name == dominant:
+                avg = dom_ms
+            else:
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)]
+                for a, b in evs:
+                    a.record(stream)
+                    c.fn()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                avg = sum(a.elapsed_time(b) for a, b in evs) / max(len(evs), 1)
             d = {"ms": round(avg, 5)}
             if c.bytes:
                 d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
@@ -320,17 +377,18 @@ def main():
             per[c.name] = d
 
         dom = next(c for c in calls if c.name == dominant)
-        dms = per[dominant]["ms"]
+        dms = dom_ms
         if bound == "hbm":
             ach = dom.bytes / (dms * 1e-3) / 1e9
             roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": None}
+                    "traffic": counter_traffic(dominant, name)}
         else:
             ach = dom.flops / (dms * 1e-3) / 1e12
             roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1),
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                    "traffic": counter_traffic(dominant, name)}
         if unit == "GB/s":
             value = sum(c.bytes for c in calls) / (ms * 1e-3) / 1e9
         else:

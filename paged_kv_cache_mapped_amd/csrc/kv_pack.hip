@@ -13,7 +13,7 @@
 // contiguous byte range in both cache layouts, so the copy is layout-agnostic.
 //
 // Pure HBM streaming: one workgroup per (block, K|V), 256 threads, each thread
-// keeps four 16-byte loads in flight before storing them.
+// keeps eight 16-byte loads in flight before storing them.
 #include "common.h"
 #include "internal.h"
 
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void pack_kernel(u32x4_t* __restrict__ kc, u32
   u32x4_t* packed = buf + ((int64_t)kv * n + i) * cpb;
   const u32x4_t* src = UNPACK ? packed : cache;
   u32x4_t* dst = UNPACK ? cache : packed;
-  constexpr int U = 4;
+  constexpr int U = 8;
   for (int32_t base = threadIdx.x; base < cpb; base += 256 * U) {
     u32x4_t r[U];
 #pragma unroll
