@@ -1,5 +1,5 @@
-// Paged decode attention for gfx950: split-K over the block table, then a
-// log-sum-exp combine of the splits.
+// Paged decode attention for gfx950: balanced split-K over the block table,
+// then a log-sum-exp combine of the pieces of each request.
 //
 // "Beyond just running: native inference optimisation in vLLM on AMD ROCm",
 // section "Every batch handles a mixed workload": a decode request produces one
@@ -10,9 +10,11 @@
 // "From LLM performance optimisation to DeepSeek deployment", section 3 "Paged
 // Attention": logical block i of a request lives in physical block table[i].
 //
-// Work split.  One workgroup (4 waves) owns (request b, KV head, group of up to
-// 16 query heads sharing it, token range of split_tokens).  Its waves take
-// interleaved 32-token tiles of the range.  Per tile a wave:
+// Work split.  The requests' lengths, rounded up to the 32-token tile, are
+// concatenated into one token stream that is cut into equal pieces.  One
+// workgroup (4 waves) owns (piece, KV head, group of up to 16 query heads
+// sharing it) and runs one segment per request its piece overlaps; its waves
+// take interleaved 32-token tiles of the segment.  Per tile a wave:
 //   * loads K rows straight into MFMA A-operand registers (16-byte loads),
 //   * computes S^T = K Q^T for its query-head group with v_mfma_f32_16x16x32_bf16
 //     (query heads are the 16 MFMA columns; grouped-query decode is a dense
@@ -25,8 +27,10 @@
 //     already stored token-minor ([block][head][bs/x][D][x]) and is loaded
 //     straight into registers.
 // The 4 waves merge their (m, l, O) in LDS; the workgroup writes either the
-// final output (single-split request) or an fp32 partial (o, lse) that a
-// second kernel merges with LSE weights.
+// final output (a request inside one piece) or an fp32 partial (o, lse) that a
+// second kernel merges with LSE weights.  (Merging in the last piece to
+// finish would need device-scope fences, which on this multi-XCD part write
+// back and invalidate whole L2 caches: far slower than a second launch.)
 //
 // fp8 (OCP e4m3fn) caches are decoded to bf16 in registers (exact) and the
 // per-tensor scales are applied to the scores (k_scale) and to the output
@@ -44,6 +48,7 @@ constexpr int kVRowBytes = 288;                  // 128 bf16 + 32 B pad (bank sp
 constexpr int kVTileBytes = kTile * kVRowBytes;  // per wave; also holds 16x128 fp32 at the end
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kTabCap = 512;                     // block ids of one split staged in LDS
+constexpr int kPlanLdsMax = 2048;                // batches up to this size plan in LDS
 
 struct DecodeArgs {
   const uint8_t* kc;
@@ -61,6 +66,7 @@ struct DecodeArgs {
   int32_t max_blocks, num_blocks, bs, bs_log2, Hkv, Hq, G, n_gchunks;
   int32_t n_slots, batch, fixed_len, len_min, len_max, target_pieces;
   int32_t max_len;            // lengths are clamped to min(table capacity, max_seq_len)
+  int32_t lds_plan;           // 1: every workgroup plans in LDS (batch <= kPlanLdsMax)
   float qk_mult;   // scale * k_scale * log2(e): scores in the exp2 domain
   float v_scale;
 };
@@ -277,12 +283,21 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Piece length from the padded stream length T (same rule in both planners).
+__device__ __forceinline__ int32_t piece_len(const DecodeArgs& a, int32_t T) {
+  if (a.fixed_len > 0) return a.fixed_len;
+  int32_t len = (T + a.target_pieces - 1) / a.target_pieces;
+  len = (len + 31) & ~31;
+  return len < a.len_min ? a.len_min : (len > a.len_max ? a.len_max : len);
+}
+
 // Work plan (one workgroup): lengths rounded up to the 32-token tile are
 // concatenated into one token stream of length T; the stream is cut into
 // pieces of equal length (a multiple of 32), so every workgroup of the main
 // kernel gets the same amount of KV to read however the lengths are spread.
 // Writes cum[] (exclusive prefix sums), the header and, for every piece, the
-// first request it touches.
+// first request it touches.  Used for batches above kPlanLdsMax; smaller
+// batches are planned by every main-pass workgroup in its own LDS.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   __shared__ int32_t s_part[1024];
   const int tid = threadIdx.x;
@@ -306,14 +321,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
     run += (clamp_len(a.seq_lens[b], cap) + 31) & ~31;
   }
   const int32_t T = s_part[1023];
-  int32_t len;
-  if (a.fixed_len > 0) {
-    len = a.fixed_len;
-  } else {
-    len = (T + a.target_pieces - 1) / a.target_pieces;
-    len = (len + 31) & ~31;
-    len = len < a.len_min ? a.len_min : (len > a.len_max ? a.len_max : len);
-  }
+  const int32_t len = piece_len(a, T);
   const int32_t NP = (T + len - 1) / len;
   if (tid == 0) {
     a.cum[B] = T;
@@ -342,6 +350,10 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 // one segment per request it overlaps.  Each segment ends with a 4-wave merge
 // and either the final output (a request covered by one piece) or an fp32
 // partial (o, lse) in slot (piece - first piece of the request).
+//
+// The plan (prefix sums of the rounded lengths, piece length, first request
+// of a piece) comes from LDS, computed by every workgroup for itself when the
+// batch is small, else from decode_plan_kernel's output in the workspace.
 template <int LAYOUT, int DT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void decode_piece_kernel(DecodeArgs a) {
@@ -359,13 +371,78 @@ void decode_piece_kernel(DecodeArgs a) {
   __shared__ float sm_m[kWaves][16];
   __shared__ float sm_l[kWaves][16];
   __shared__ int32_t s_tab[kTabCap];
+  __shared__ int32_t s_cum[kPlanLdsMax + 1];
+  __shared__ int32_t s_wsum[kWaves];
   uint8_t* vt = smem + wave * kVTileBytes;
 
-  const int32_t T = a.hdr[0], len = a.hdr[1], NP = a.hdr[2];
+  int32_t T, len, NP;
+  if (a.lds_plan) {
+    // exclusive prefix sums of the rounded lengths: 8 requests per thread,
+    // a wave scan, then the 4 wave totals
+    constexpr int kPer = kPlanLdsMax / 256;
+    const int32_t b0 = (int32_t)threadIdx.x * kPer;
+    int32_t v[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      v[i] = b0 + i < a.batch ? (clamp_len(a.seq_lens[b0 + i], cap) + 31) & ~31 : 0;
+      sum += v[i];
+    }
+    int32_t inc = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int32_t run = inc - sum;
+    T = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      run += w < wave ? s_wsum[w] : 0;
+      T += s_wsum[w];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (b0 + i < a.batch) s_cum[b0 + i] = run;
+      run += v[i];
+    }
+    if (threadIdx.x == 0) s_cum[a.batch] = T;
+    __syncthreads();
+    len = piece_len(a, T);
+    NP = (T + len - 1) / len;
+    if (blockIdx.x == 0 && blockIdx.y == 0) {   // the plan the combine pass reads
+      for (int32_t b = threadIdx.x; b <= a.batch; b += 256) a.cum[b] = s_cum[b];
+      if (threadIdx.x == 0) {
+        a.hdr[0] = T;
+        a.hdr[1] = len;
+        a.hdr[2] = NP;
+      }
+    }
+  } else {
+    T = a.hdr[0];
+    len = a.hdr[1];
+    NP = a.hdr[2];
+  }
+  auto cum_at = [&](int32_t b) -> int32_t { return a.lds_plan ? s_cum[b] : a.cum[b]; };
+
   for (int32_t p = blockIdx.x; p < NP; p += gridDim.x) {
     const int32_t pstart = p * len, pend = min(T, pstart + len);
-    for (int32_t b = a.first_seq[p]; b < a.batch; ++b) {
-      const int32_t cb = a.cum[b];
+    int32_t b_first;
+    if (a.lds_plan) {
+      // largest b with cum[b] <= pstart (empty requests share their
+      // successor's offset, so the largest one is non-empty)
+      int32_t lo = 0, hi = a.batch - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= pstart) lo = mid; else hi = mid - 1;
+      }
+      b_first = lo;
+    } else {
+      b_first = a.first_seq[p];
+    }
+    for (int32_t b = b_first; b < a.batch; ++b) {
+      const int32_t cb = cum_at(b);
       if (cb >= pend) break;
       const int32_t L = clamp_len(a.seq_lens[b], cap);
       const int32_t t_begin = max(pstart, cb) - cb;      // multiple of 32
@@ -492,15 +569,34 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int32_t n_b = (cb + L - 1) / len - cb / len + 1;
   if (n_b <= 1) return;                      // written by the main pass
   const float* pl = a.part_lse + bh * a.n_slots;
+  const f32x2_t* po = (const f32x2_t*)(a.part_o + bh * a.n_slots * kD) + lane;
   float M = kNegInf;
-  for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i]);
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
-  const f32x2_t* po = (const f32x2_t*)(a.part_o + bh * a.n_slots * kD) + lane;
-  for (int i = 0; i < n_b; ++i) {
-    const float w = fast_exp2((pl[i] - M) * kLog2e);
-    wsum += w;
-    acc += w * po[i * (kD / 2)];
+  constexpr int kU = 8;
+  if (n_b <= kU) {                  // common case: every load issued up front
+    float lv[kU];
+    f32x2_t ov[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      lv[i] = i < n_b ? pl[i] : kNegInf;
+      ov[i] = i < n_b ? po[i * (kD / 2)] : f32x2_t{0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i) M = fmaxf(M, lv[i]);
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const float w = i < n_b ? fast_exp2((lv[i] - M) * kLog2e) : 0.f;
+      wsum += w;
+      acc += w * ov[i];
+    }
+  } else {
+    for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i]);
+    for (int i = 0; i < n_b; ++i) {
+      const float w = fast_exp2((pl[i] - M) * kLog2e);
+      wsum += w;
+      acc += w * po[i * (kD / 2)];
+    }
   }
   const float inv = 1.f / wsum;
   const __bf16 o0 = (__bf16)(acc[0] * inv), o1 = (__bf16)(acc[1] * inv);
@@ -554,6 +650,7 @@ size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_
          align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
 
+
 hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
                          int32_t batch, int32_t num_q_heads, const int32_t* tables,
                          int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
@@ -595,9 +692,13 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   a.target_pieces = p.pieces_per_group;
   a.qk_mult = scale * c.k_scale * kLog2e;
   a.v_scale = c.v_scale;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  a.lds_plan = batch <= kPlanLdsMax ? 1 : 0;
+  hipError_t e;
+  if (!a.lds_plan) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((unsigned)p.pieces_per_group, (unsigned)(c.num_kv_heads * p.n_gchunks));
 #define PKV_LAUNCH(L, T) \
   hipLaunchKernelGGL((decode_piece_kernel<L, T>), grid, dim3(256), 0, s, a)

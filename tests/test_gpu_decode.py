@@ -91,6 +91,54 @@ def test_decode_split_invariance_and_determinism():
         ref = (out, lse)
 
 
+@pytest.mark.parametrize("batch", [2048, 2300])
+def test_decode_large_batch_plans(batch):
+    """Batches of up to 2048 requests are planned by every workgroup in its own
+    LDS, larger ones by the separate planning kernel; both agree with the
+    oracle (short, skewed lengths: many requests per piece)."""
+    st = w.decode_workload(12, batch, 8, 2, 128, 16, batch * 9 + 64, 1, 120,
+                           fixed_lens=[1, 2, 120, 31, 32, 33])
+    w.poison_cache(st.cache, st.block_tables, st.seq_lens)
+    say(f"decode batch={batch}")
+    dc = device_cache(st.cache)
+    out, lse = _run(dc, st)
+    rows = list(range(8)) + list(np.random.default_rng(3).choice(batch, 200, replace=False))
+    rows += [batch - 1]
+    _check(st, oracle_cache(st.cache), out, lse, BF16_TOL, rows)
+    out_s, lse_s = _run(dc, st, split=64)     # many pieces per request
+    _check(st, oracle_cache(st.cache), out_s, lse_s, BF16_TOL, rows)
+
+
+def test_decode_workspace_reuse_with_stale_contents():
+    """The plan and the partial slots live in the caller's workspace: calls of
+    different shapes on one workspace that starts out as random bytes must each
+    produce the oracle's result, and repeated calls bit-identical ones."""
+    t = torch()
+    big = w.decode_workload(13, 24, 32, 4, 128, 16, 24 * 260 + 64, 500, 4000)
+    small = w.decode_workload(14, 5, 16, 2, 128, 16, 5 * 80 + 64, 300, 1200)
+    dcb, dcs = device_cache(big.cache), device_cache(small.cache)
+    need = max(pk.paged_decode_workspace_bytes(dcb, 24, 32, int(big.seq_lens.max()), 128),
+               pk.paged_decode_workspace_bytes(dcs, 5, 16, int(small.seq_lens.max()), 128))
+    ws = t.randint(0, 256, (need,), dtype=t.uint8, device="cuda")
+    say("decode workspace reuse")
+
+    def run(dc, st, split):
+        out, lse = pk.paged_decode(dc, dev(st.q), dev(st.block_tables), dev(st.seq_lens),
+                                   int(st.seq_lens.max()), st.scale, workspace=ws,
+                                   split_tokens=split)
+        t.cuda.synchronize()
+        return bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+    ob_, os_ = oracle_cache(big.cache), oracle_cache(small.cache)
+    first = run(dcb, big, 128)
+    _check(big, ob_, *first, BF16_TOL)
+    for split in (128, 0, 256):
+        o, l = run(dcs, small, split)
+        _check(small, os_, o, l, BF16_TOL)
+    again = run(dcb, big, 128)
+    assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
 def test_decode_needle():
     """One planted key with a dominant score: the output must be its value row
     (catches a mis-gathered block, which random data would hide)."""
