@@ -17,6 +17,20 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Index of the calling wave in its workgroup, as a value the compiler knows
+// to be wave-uniform (an SGPR): loops bounded by it are then plain scalar
+// loops instead of exec-masked divergent ones, whose merged exits make the
+// compiler wait on loads still in flight.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// A value every lane of the wave holds identically (read from LDS or global
+// memory at a uniform address), moved to an SGPR for the same reason.
+__device__ __forceinline__ int32_t uniform(int32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
 // v_mfma_f32_16x16x32_bf16.  Lane l = 16*q + r supplies A[row r][k 8q..8q+7]
 // and B[k 8q..8q+7][col r]; it receives C[rows 4q..4q+3][col r].
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {

@@ -164,7 +164,7 @@ struct RowState {
 // the running state.
 __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t qbase, int32_t q0,
                                           int32_t qn, RowState& S) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;
   const int32_t row = q0 + 32 * wave + r;
   // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
@@ -189,7 +189,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
                                          int32_t q0, int32_t qn, int32_t k_begin, int32_t k_end,
                                          RowState& S) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
   const int32_t row = q0 + 32 * wave + r;       // this lane's query row (in sequence)
@@ -315,7 +315,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 template <bool PARTIAL>
 __device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_t qbase,
                                             int32_t q0, int32_t qn, int32_t part, RowState& S) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;
   const int32_t row = q0 + 32 * wave + r;
   const float l_run = S.l_run + __shfl_xor(S.l_run, 32);
@@ -473,7 +473,7 @@ void extend_fused_kernel(AttnArgs a) {
 // o = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p - max_p lse_p),
 // lse = max + ln sum_p w_p.
 __global__ __launch_bounds__(256) void extend_merge_kernel(AttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
   if (rh >= (int64_t)a.rows * a.Hq) return;
   const int32_t grow = (int32_t)(rh / a.Hq);

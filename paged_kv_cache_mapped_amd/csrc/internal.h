@@ -33,7 +33,8 @@ struct DecodePlan {
   int32_t n_gchunks;         // ceil(G / 16) groups of query heads per KV head
   int32_t fixed_len;         // piece length if fixed, else 0
   int32_t len_min, len_max;  // bounds of the automatic piece length
-  int32_t pieces_per_group;  // grid x: workgroups per (KV head, query-head group)
+  int32_t pieces_per_group;  // grid x: workgroups along the token stream
+  int32_t gpw;               // head groups per workgroup (1, 2 or 4)
   int32_t n_slots;           // partial slots per (request, head)
   int32_t max_pieces;        // upper bound of the number of pieces
 };

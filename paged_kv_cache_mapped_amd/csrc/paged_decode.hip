@@ -11,10 +11,10 @@
 // Attention": logical block i of a request lives in physical block table[i].
 //
 // Work split.  The requests' lengths, rounded up to the 32-token tile, are
-// concatenated into one token stream that is cut into equal pieces.  One
-// workgroup (4 waves) owns (piece, KV head, group of up to 16 query heads
-// sharing it) and runs one segment per request its piece overlaps; its waves
-// take interleaved 32-token tiles of the segment.  Per tile a wave:
+// concatenated into one token stream that is cut into equal pieces.  Every
+// wave is an independent worker that owns (piece, KV head, group of up to 16
+// query heads sharing it) and runs one segment per request its piece
+// overlaps, streaming the segment's 32-token tiles.  Per tile the wave:
 //   * loads K rows straight into MFMA A-operand registers (16-byte loads),
 //   * computes S^T = K Q^T for its query-head group with v_mfma_f32_16x16x32_bf16
 //     (query heads are the 16 MFMA columns; grouped-query decode is a dense
@@ -22,15 +22,15 @@
 //   * runs the online softmax in registers (per query head: max / sum over the
 //     4 lanes holding its 32 scores via cross-lane shuffles),
 //   * accumulates O^T = V^T P^T with V^T as the A operand.  In the NHD layout V
-//     rows are staged in LDS with 16-byte coalesced stores and read back
-//     transposed with ds_read_b64_tr_b16; in the preshuffled layout V is
-//     already stored token-minor ([block][head][bs/x][D][x]) and is loaded
+//     rows are staged in the wave's LDS rows with 16-byte coalesced stores and
+//     read back transposed with ds_read_b64_tr_b16; in the preshuffled layout V
+//     is already stored token-minor ([block][head][bs/x][D][x]) and is loaded
 //     straight into registers.
-// The 4 waves merge their (m, l, O) in LDS; the workgroup writes either the
-// final output (a request inside one piece) or an fp32 partial (o, lse) that a
-// second kernel merges with LSE weights.  (Merging in the last piece to
-// finish would need device-scope fences, which on this multi-XCD part write
-// back and invalidate whole L2 caches: far slower than a second launch.)
+// At the end of a segment the wave writes either the final output (a request
+// inside one piece) or an fp32 partial (o, lse) that a second kernel merges
+// with LSE weights.  (Merging in the last piece to finish would need
+// device-scope fences, which on this multi-XCD part write back and invalidate
+// whole L2 caches: far slower than a second launch.)
 //
 // fp8 (OCP e4m3fn) caches are decoded to bf16 in registers (exact) and the
 // per-tensor scales are applied to the scores (k_scale) and to the output
@@ -43,11 +43,12 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kTile = 32;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                        // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kVRowBytes = 288;                  // 128 bf16 + 32 B pad (bank spread)
-constexpr int kVTileBytes = kTile * kVRowBytes;  // per wave; also holds 16x128 fp32 at the end
+constexpr int kVTileBytes = kTile * kVRowBytes;  // per wave
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kTabCap = 512;                     // block ids of one split staged in LDS
+constexpr int kTabCap = 256;                     // block ids of one wave's segment staged in LDS
 constexpr int kPlanLdsMax = 2048;                // batches up to this size plan in LDS
 
 struct DecodeArgs {
@@ -67,6 +68,7 @@ struct DecodeArgs {
   int32_t n_slots, batch, fixed_len, len_min, len_max, target_pieces;
   int32_t max_len;            // lengths are clamped to min(table capacity, max_seq_len)
   int32_t lds_plan;           // 1: every workgroup plans in LDS (batch <= kPlanLdsMax)
+  int32_t gpw;                // head groups per workgroup (1, 2 or 4); 4 / gpw waves share a group
   float qk_mult;   // scale * k_scale * log2(e): scores in the exp2 domain
   float v_scale;
 };
@@ -246,7 +248,7 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
   for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
   mt = fmaxf(mt, __shfl_xor(mt, 16));
   mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const float m_new = fmaxf(st.m, mt);      // finite: every tile has a valid token
+  const float m_new = fmaxf(st.m, mt);      // finite: a wave's first tile has a valid token
   const float alpha = fast_exp2(st.m - m_new);
   float p[8], psum = 0.f;
 #pragma unroll
@@ -345,22 +347,32 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   }
 }
 
-// Main pass: workgroup (p, group) walks pieces p, p + gridDim.x, ... of the
-// token stream for its (KV head, query-head group); inside a piece it runs
-// one segment per request it overlaps.  Each segment ends with a 4-wave merge
-// and either the final output (a request covered by one piece) or an fp32
-// partial (o, lse) in slot (piece - first piece of the request).
+// Main pass.  Every wave is an independent worker for one (KV head,
+// query-head group): the workgroup's gpw groups are consecutive, and the
+// 4 / gpw waves of one group take pieces x*(4/gpw) + sub, stepping by
+// gridDim.x * (4/gpw).  With gpw = 4 the four waves of a CU read four heads of
+// the same tokens at about the same time (1 KB of each token's K and V rows
+// instead of four scattered 256-byte slices), which keeps DRAM rows open.
+// For each request its piece overlaps, a wave stages the segment's block ids in its own LDS slice,
+// streams the segment's 32-token tiles through a two-deep register pipeline,
+// and writes either the final output (a request covered by one piece) or an
+// fp32 partial (o, lse) in slot (piece - first piece of the request).  No
+// barrier is taken after the plan, so the waves of a CU drift apart and each
+// one's request boundaries are covered by the others' streaming.
 //
 // The plan (prefix sums of the rounded lengths, piece length, first request
 // of a piece) comes from LDS, computed by every workgroup for itself when the
 // batch is small, else from decode_plan_kernel's output in the workspace.
 template <int LAYOUT, int DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void decode_piece_kernel(DecodeArgs a) {
-  const int32_t hkv = blockIdx.y / a.n_gchunks;
-  const int32_t gc = blockIdx.y - hkv * a.n_gchunks;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
+  const int wpg = kWaves / a.gpw;                  // waves per head group
+  const int32_t grp = blockIdx.y * a.gpw + wave % a.gpw;
+  const int sub = wave / a.gpw;
+  const int32_t hkv = grp / a.n_gchunks;
+  const int32_t gc = grp - hkv * a.n_gchunks;
   const int q4 = lane >> 4, r = lane & 15;
   const int g0 = gc * 16;
   const int gcnt = min(16, a.G - g0);
@@ -368,18 +380,26 @@ void decode_piece_kernel(DecodeArgs a) {
   const int32_t cap = a.max_len;
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * kVTileBytes];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ int32_t s_tab[kTabCap];
+  __shared__ int32_t s_tab[kWaves][kTabCap];
   __shared__ int32_t s_cum[kPlanLdsMax + 1];
   __shared__ int32_t s_wsum[kWaves];
+  __shared__ int32_t s_prog[kWaves];     // tiles consumed so far, per wave
   uint8_t* vt = smem + wave * kVTileBytes;
+  int32_t* tab = s_tab[wave];
+
+  // Waves w and w ^ 4 share a SIMD, and its arbiter favours the older one:
+  // left alone, waves 0-3 finish their (equal) pieces far ahead of waves 4-7
+  // and the SIMD then streams with half the loads in flight.  Each wave
+  // publishes its progress and raises its priority while it trails its
+  // partner, which keeps the pair level.
+  int32_t my_prog = 0;
+  if (lane == 0) s_prog[wave] = 0;
 
   int32_t T, len, NP;
   if (a.lds_plan) {
     // exclusive prefix sums of the rounded lengths: 8 requests per thread,
     // a wave scan, then the 4 wave totals
-    constexpr int kPer = kPlanLdsMax / 256;
+    constexpr int kPer = kPlanLdsMax / kThreads;
     const int32_t b0 = (int32_t)threadIdx.x * kPer;
     int32_t v[kPer], sum = 0;
 #pragma unroll
@@ -409,10 +429,11 @@ void decode_piece_kernel(DecodeArgs a) {
     }
     if (threadIdx.x == 0) s_cum[a.batch] = T;
     __syncthreads();
+    T = uniform(T);
     len = piece_len(a, T);
     NP = (T + len - 1) / len;
     if (blockIdx.x == 0 && blockIdx.y == 0) {   // the plan the combine pass reads
-      for (int32_t b = threadIdx.x; b <= a.batch; b += 256) a.cum[b] = s_cum[b];
+      for (int32_t b = threadIdx.x; b <= a.batch; b += kThreads) a.cum[b] = s_cum[b];
       if (threadIdx.x == 0) {
         a.hdr[0] = T;
         a.hdr[1] = len;
@@ -420,13 +441,14 @@ void decode_piece_kernel(DecodeArgs a) {
       }
     }
   } else {
-    T = a.hdr[0];
-    len = a.hdr[1];
-    NP = a.hdr[2];
+    T = uniform(a.hdr[0]);
+    len = uniform(a.hdr[1]);
+    NP = uniform(a.hdr[2]);
+    __syncthreads();                          // s_prog is initialised
   }
   auto cum_at = [&](int32_t b) -> int32_t { return a.lds_plan ? s_cum[b] : a.cum[b]; };
 
-  for (int32_t p = blockIdx.x; p < NP; p += gridDim.x) {
+  for (int32_t p = blockIdx.x * wpg + sub; p < NP; p += gridDim.x * wpg) {
     const int32_t pstart = p * len, pend = min(T, pstart + len);
     int32_t b_first;
     if (a.lds_plan) {
@@ -437,14 +459,14 @@ void decode_piece_kernel(DecodeArgs a) {
         const int32_t mid = (lo + hi + 1) >> 1;
         if (s_cum[mid] <= pstart) lo = mid; else hi = mid - 1;
       }
-      b_first = lo;
+      b_first = uniform(lo);
     } else {
-      b_first = a.first_seq[p];
+      b_first = uniform(a.first_seq[p]);
     }
     for (int32_t b = b_first; b < a.batch; ++b) {
-      const int32_t cb = cum_at(b);
+      const int32_t cb = uniform(cum_at(b));
       if (cb >= pend) break;
-      const int32_t L = clamp_len(a.seq_lens[b], cap);
+      const int32_t L = uniform(clamp_len(a.seq_lens[b], cap));
       const int32_t t_begin = max(pstart, cb) - cb;      // multiple of 32
       const int32_t t_end = min(pend - cb, L);
       if (t_begin >= t_end) continue;                    // only padding of b
@@ -452,12 +474,16 @@ void decode_piece_kernel(DecodeArgs a) {
       const int32_t n_b = (cb + L - 1) / len - first_piece + 1;
       const int32_t slot = p - first_piece;
 
-      // segment prologue: table slice and Q, issued together
+      // segment prologue: this wave's block-id slice and Q, issued together.
+      // The slice goes to the wave's own LDS rows; a wave's LDS accesses
+      // complete in order, so no barrier is needed before reading them.
       const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
       const int32_t ib0 = t_begin >> a.bs_log2;
       const int32_t nent = ((t_end - 1) >> a.bs_log2) - ib0 + 1;   // <= kTabCap
-      const int32_t tb0 = (int32_t)threadIdx.x < nent ? trow[ib0 + threadIdx.x] : 0;
-      const int32_t tb1 = (int32_t)threadIdx.x + 256 < nent ? trow[ib0 + threadIdx.x + 256] : 0;
+      int32_t tb[kTabCap / 64];
+#pragma unroll
+      for (int j = 0; j < kTabCap / 64; ++j)
+        tb[j] = lane + 64 * j < nent ? trow[ib0 + lane + 64 * j] : 0;
       bf16x8_t qb[4];
       {
         const bf16x8_t zero = {};
@@ -466,10 +492,10 @@ void decode_piece_kernel(DecodeArgs a) {
         for (int kk = 0; kk < 4; ++kk)
           qb[kk] = (r < gcnt) ? *(const bf16x8_t*)(qrow + dmap<DT>(kk, q4)) : zero;
       }
-      __syncthreads();                   // previous segment's LDS readers are done
-      if ((int32_t)threadIdx.x < nent) s_tab[threadIdx.x] = clamp_block(tb0, a.num_blocks);
-      if ((int32_t)threadIdx.x + 256 < nent) s_tab[threadIdx.x + 256] = clamp_block(tb1, a.num_blocks);
-      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kTabCap / 64; ++j)
+        if (lane + 64 * j < nent) tab[lane + 64 * j] = clamp_block(tb[j], a.num_blocks);
+      order_lds();
 
       WaveState st;
 #pragma unroll
@@ -477,77 +503,52 @@ void decode_piece_kernel(DecodeArgs a) {
       st.m = kNegInf;
       st.l = 0.f;
 
-      // Tiles of this wave: wave, wave + 4, ...  Two register buffers: the
-      // next tile's loads are in flight while the current tile is consumed
-      // (the scheduling barriers keep the compiler from sinking them).
+      // Two register buffers: the next tile's loads are in flight while the
+      // current tile is consumed (the scheduling barriers keep the compiler
+      // from sinking them).  Tiles go in pairs: a second tile past the end has
+      // every token masked (scores -inf, weights 0, rows clamped to the last
+      // valid token) and changes nothing.  An early exit between the two
+      // halves would leave the second buffer's loads in flight on one path
+      // into the loop head, and the compiler then waits on them there in
+      // every iteration, which serialises the prefetch.
       const int32_t n_tiles = (t_end - t_begin + kTile - 1) / kTile;
       TileRaw A, B;
-      issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + wave * kTile, t_end, lane, A);
-      for (int32_t it = wave; it < n_tiles; it += 2 * kWaves) {
-        issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + (it + kWaves) * kTile, t_end, lane, B);
+      issue_tile<LAYOUT, DT>(a, tab, ib0, hkv, t_begin, t_end, lane, A);
+      for (int32_t it = 0; it < n_tiles; it += 2) {
+        my_prog += 2;
+        if (lane == 0) s_prog[wave] = my_prog;
+        if (my_prog <= uniform(s_prog[wave ^ 4])) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(0);
+        issue_tile<LAYOUT, DT>(a, tab, ib0, hkv, t_begin + (it + 1) * kTile, t_end, lane, B);
         __builtin_amdgcn_sched_barrier(0);
         consume_tile<LAYOUT, DT>(a, A, qb, t_begin + it * kTile, t_end, lane, vt, st);
-        if (it + kWaves >= n_tiles) break;
-        issue_tile<LAYOUT, DT>(a, s_tab, ib0, hkv, t_begin + (it + 2 * kWaves) * kTile, t_end, lane, A);
+        issue_tile<LAYOUT, DT>(a, tab, ib0, hkv, t_begin + (it + 2) * kTile, t_end, lane, A);
         __builtin_amdgcn_sched_barrier(0);
-        consume_tile<LAYOUT, DT>(a, B, qb, t_begin + (it + kWaves) * kTile, t_end, lane, vt, st);
+        consume_tile<LAYOUT, DT>(a, B, qb, t_begin + (it + 1) * kTile, t_end, lane, vt, st);
       }
+      __builtin_amdgcn_s_waitcnt(0);     // the last prefetch (past the end) lands
 
-      // ---- merge the 4 waves
-      float l_run = st.l;
-      l_run += __shfl_xor(l_run, 16);
-      l_run += __shfl_xor(l_run, 32);
-      if (q4 == 0) {
-        sm_m[wave][r] = st.m;
-        sm_l[wave][r] = l_run;
-      }
-      __syncthreads();
-      float M = kNegInf;
+      // ---- this wave's result for the segment: query head r, dims 16n + 4*q4 + i
+      float l_sum = st.l;
+      l_sum += __shfl_xor(l_sum, 16);
+      l_sum += __shfl_xor(l_sum, 32);
+      if (r < gcnt) {
+        const int64_t bh = (int64_t)b * a.Hq + h_base + r;
+        const float f = a.v_scale / l_sum;       // l_sum > 0: the segment has a token
+        const float lse_v = (st.m + __log2f(l_sum)) * kLn2;
+        if (n_b == 1) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
-      float Lt = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_m[w][r];
-        Lt += (mw == kNegInf) ? 0.f : sm_l[w][r] * fast_exp2(mw - M);
-      }
-      const float f = (st.m == kNegInf || !(Lt > 0.f)) ? 0.f : fast_exp2(st.m - M) / Lt;
-      float* ob = (float*)vt;            // [16 heads][128 dims] fp32
-#pragma unroll
-      for (int n = 0; n < 8; ++n) *(f32x4_t*)(ob + r * kD + 16 * n + 4 * q4) = st.o[n] * f;
-      __syncthreads();
-
-      const bool final_out = (n_b == 1);
-      for (int idx = threadIdx.x; idx < gcnt * (kD / 4); idx += 256) {
-        const int g = idx / (kD / 4), d4 = idx - g * (kD / 4);
-        f32x4_t s4 = *(const f32x4_t*)((const float*)smem + g * kD + 4 * d4);
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-          s4 += *(const f32x4_t*)((const float*)(smem + w * kVTileBytes) + g * kD + 4 * d4);
-        s4 *= a.v_scale;
-        const int64_t bh = (int64_t)b * a.Hq + h_base + g;
-        if (final_out) {
-          const bf16x4_t v4 = {(__bf16)s4[0], (__bf16)s4[1], (__bf16)s4[2], (__bf16)s4[3]};
-          *(bf16x4_t*)(a.out + bh * kD + 4 * d4) = v4;
+          for (int n = 0; n < 8; ++n) {
+            const f32x4_t o = st.o[n] * f;
+            const bf16x4_t v4 = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+            *(bf16x4_t*)(a.out + bh * kD + 16 * n + 4 * q4) = v4;
+          }
+          if (q4 == 0 && a.lse) a.lse[bh] = lse_v;
         } else {
-          *(f32x4_t*)(a.part_o + (bh * a.n_slots + slot) * kD + 4 * d4) = s4;
-        }
-      }
-      if ((int)threadIdx.x < gcnt) {
-        const int g = threadIdx.x;
-        float Mg = kNegInf;
-        for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, sm_m[w][g]);
-        float Lg = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
-          const float mw = sm_m[w][g];
-          Lg += (mw == kNegInf) ? 0.f : sm_l[w][g] * fast_exp2(mw - Mg);
-        }
-        const float lse_v = (Mg + __log2f(Lg)) * kLn2;
-        const int64_t bh = (int64_t)b * a.Hq + h_base + g;
-        if (final_out) {
-          if (a.lse) a.lse[bh] = lse_v;
-        } else {
-          a.part_lse[bh * a.n_slots + slot] = lse_v;
+          float* po = a.part_o + (bh * a.n_slots + slot) * kD;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) *(f32x4_t*)(po + 16 * n + 4 * q4) = st.o[n] * f;
+          if (q4 == 0) a.part_lse[bh * a.n_slots + slot] = lse_v;
         }
       }
     }
@@ -558,7 +559,7 @@ void decode_piece_kernel(DecodeArgs a) {
 // lse = max + ln sum_i w_i, over the pieces of each request that spans more
 // than one piece.  One wave per (request, query head).
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
   if (bh >= (int64_t)a.batch * a.Hq) return;
   const int32_t b = (int32_t)(bh / a.Hq);
@@ -619,7 +620,7 @@ DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
   const int32_t G = num_q_heads / c.num_kv_heads;
   p.n_gchunks = (G + 15) / 16;
   const int32_t groups = c.num_kv_heads * p.n_gchunks;
-  // a piece's block ids must fit the LDS table: len/bs + 1 <= kTabCap
+  // a piece's block ids must fit a wave's LDS slice: len/bs + 1 <= kTabCap
   int64_t len_max = ((int64_t)(kTabCap - 1) << log2_ceil(c.block_size)) & ~(int64_t)31;
   if (len_max > 16384) len_max = 16384;
   p.len_max = (int32_t)len_max;
@@ -630,9 +631,13 @@ DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
     p.fixed_len = 0;
     p.len_min = 256 < p.len_max ? 256 : p.len_max;
   }
-  // grid: two rounds of two resident workgroups per CU, shared by the groups
-  const int32_t slots = device_cu_count() * 2 * 2;
-  p.pieces_per_group = slots / groups > 0 ? slots / groups : 1;
+  // head groups per workgroup: as many of the 8 as divide evenly, so a
+  // workgroup's waves read the heads of the same tokens together
+  p.gpw = groups % 8 == 0 ? 8 : (groups % 4 == 0 ? 4 : (groups % 2 == 0 ? 2 : 1));
+  // grid: one round of one resident workgroup per CU
+  const int32_t slots = device_cu_count();
+  const int32_t rows = groups / p.gpw;
+  p.pieces_per_group = slots / rows > 0 ? slots / rows : 1;   // grid x
   p.split_tokens = p.fixed_len;
   p.n_slots = (max_seq_len + p.len_min - 1) / p.len_min + 1;
   const int64_t padded = (int64_t)batch * ((max_seq_len + 31) & ~31);
@@ -689,7 +694,8 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   a.fixed_len = p.fixed_len;
   a.len_min = p.len_min;
   a.len_max = p.len_max;
-  a.target_pieces = p.pieces_per_group;
+  a.gpw = p.gpw;
+  a.target_pieces = p.pieces_per_group * (kWaves / p.gpw);
   a.qk_mult = scale * c.k_scale * kLog2e;
   a.v_scale = c.v_scale;
   a.lds_plan = batch <= kPlanLdsMax ? 1 : 0;
@@ -699,9 +705,9 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)p.pieces_per_group, (unsigned)(c.num_kv_heads * p.n_gchunks));
+  dim3 grid((unsigned)p.pieces_per_group, (unsigned)(c.num_kv_heads * p.n_gchunks / p.gpw));
 #define PKV_LAUNCH(L, T) \
-  hipLaunchKernelGGL((decode_piece_kernel<L, T>), grid, dim3(256), 0, s, a)
+  hipLaunchKernelGGL((decode_piece_kernel<L, T>), grid, dim3(kThreads), 0, s, a)
   if (c.layout == KV_LAYOUT_NHD) {
     if (c.dtype == KV_DTYPE_BF16) PKV_LAUNCH(KV_LAYOUT_NHD, KV_DTYPE_BF16);
     else PKV_LAUNCH(KV_LAYOUT_NHD, KV_DTYPE_FP8_E4M3);
