@@ -18,6 +18,13 @@ over one batch of seeded synthetic input that is already resident in HBM:
       4 extends (512 new on 2000 cached), 2 prefills of 2000, all causal.
       Step = kv_write of all 6096 rows + paged_decode + extend_attn +
       prefill_attn.  value = query tokens / step time (tokens/s).
+  fp8_preshuffled_decode: batch 128, 64:4 heads, fp8 e4m3 KV with per-tensor
+      scales in the preshuffled layout (x = 16), context lengths uniform in
+      [1000, 16000].  Step = kv_write (quantising) + paged_decode.
+      value = algorithmic HBM bytes / step time (GB/s).
+  long_context_extend: 2 x (100000 cached + 8192 new) tokens, 64:8 heads.
+The default run measures the headline and then, as "secondary" entries, the
+mixed batch and the fp8 preshuffled decode.
 
 Roofline: the dominant call's algorithmic bytes (or flops) per launch divided
 by its average duration, from HIP events recorded around it in every timed
@@ -283,10 +290,61 @@ def build_long_context_extend(torch, pk, w, dev):
     return calls, "extend_attn", "mfma", config, cpu_sample, ("tokens/s", T)
 
 
+def build_fp8_preshuffled_decode(torch, pk, w, dev):
+    st = w.fp8_preshuffled_decode()
+    sp = st.cache.spec
+    dc = pk.PagedKVCache(dev(st.cache.k), dev(st.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim, sp.layout, sp.dtype, st.cache.k_scale, st.cache.v_scale)
+    q, kn, vn = dev(st.q), dev(st.k_new), dev(st.v_new)
+    slots, tables, lens = dev(st.slot_mapping), dev(st.block_tables), dev(st.seq_lens)
+    msl = int(st.seq_lens.max())
+    B, Hq, D, Hkv = st.batch, st.num_q_heads, sp.head_dim, sp.num_kv_heads
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(pk.paged_decode_workspace_bytes(dc, B, Hq, msl), 16), dtype=torch.uint8,
+                     device=q.device)
+    row = Hkv * D                                         # fp8: one byte per element
+    write_bytes = B * (2 * Hkv * D * 2 + 2 * row + 8)
+    kv_bytes = float(st.seq_lens.astype(np.int64).sum()) * row * 2
+    blocks = float(((st.seq_lens + 15) // 16).sum())
+    decode_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4 + blocks * 4 + B * 4
+    decode_flops = float(st.seq_lens.astype(np.int64).sum()) * Hq * 4 * D
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), write_bytes),
+        Call("paged_decode", lambda: pk.paged_decode(dc, q, tables, lens, msl, st.scale, out=out,
+                                                     lse=lse, workspace=ws),
+             decode_bytes, decode_flops),
+    ]
+    config = {
+        "workload": "fp8 e4m3 preshuffled decode: batch 128, 64:4 heads, head_dim 128, block 16, "
+                    "x 16, ctx U[1000,16000], per-tensor scales, q/out bf16",
+        "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
+        "kv_tokens": int(st.seq_lens.sum()),
+    }
+
+    def cpu_sample(budget_s=12.0):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.Cache(st.cache.k, st.cache.v, "preshuffled", "fp8", 16, Hkv, D, 16,
+                          st.cache.k_scale, st.cache.v_scale)
+        qf = ob.to_f64(st.q)
+        done, t0, nreq = 0.0, time.perf_counter(), 0
+        while time.perf_counter() - t0 < budget_s:
+            b = nreq % B
+            oa.paged_decode(qf[b:b + 1], ocache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
+                            st.scale)
+            done += float(st.seq_lens[b]) * row * 2 + 2 * Hq * D * 2
+            nreq += 1
+        t1 = time.perf_counter()
+        return done / (t1 - t0) / 1e9, f"oracle decode of {nreq} requests of this batch; {t1 - t0:.1f} s"
+
+    return calls, "paged_decode", "hbm", config, cpu_sample, ("GB/s", None)
+
+
 WORKLOADS = {
     "long_context_extend": build_long_context_extend,
     "llama70b_decode_layer": build_llama70b_decode_layer,
     "qwen3_mixed_batch": build_qwen3_mixed_batch,
+    "fp8_preshuffled_decode": build_fp8_preshuffled_decode,
 }
 
 
@@ -417,6 +475,11 @@ def main():
         r = measure("qwen3_mixed_batch", False)
         secondary["qwen3_mixed_batch"] = {
             "metric": "mixed-batch attention tokens/s", "value": round(r["value"], 1),
+            "unit": r["unit"], "ms_per_step": round(r["ms"], 4), "config": r["config"],
+            "roofline": r["roofline"], "calls": r["calls"]}
+        r = measure("fp8_preshuffled_decode", False)
+        secondary["fp8_preshuffled_decode"] = {
+            "metric": "paged decode HBM GB/s (fp8 preshuffled cache)", "value": round(r["value"], 1),
             "unit": r["unit"], "ms_per_step": round(r["ms"], 4), "config": r["config"],
             "roofline": r["roofline"], "calls": r["calls"]}
     value, unit, ms, config = main_r["value"], main_r["unit"], main_r["ms"], main_r["config"]
