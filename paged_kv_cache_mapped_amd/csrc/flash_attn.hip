@@ -66,17 +66,43 @@ struct AttnArgs {
   float* part_lse;          // [n_parts][rows][Hq]
   int32_t max_blocks, num_blocks, bs, bs_log2;
   int32_t Hq, Hkv, G, num_seqs, n_qtiles, n_parts, chunk_tokens, rows;
-  int64_t items;            // logical work items
+  int64_t items;            // lanes (work items = lanes x query tiles)
   int64_t grid_pad;         // launched workgroups (multiple of 8)
+  int32_t qt_major;         // work order inside an XCD's block of lanes
   float qk_mult;            // scale * log2(e)
 };
 
-// Launched workgroup L runs on XCD L % 8.  Give each XCD a contiguous range of
-// the logical item order, so workgroups sharing a KV head (and its K/V tiles)
-// share that XCD's L2.
-__device__ __forceinline__ int64_t logical_item(const AttnArgs& a) {
+// Work order.  A work item is (lane, query tile), lanes being the
+// (sequence[, part], KV head, query head) combinations in that order.
+// Launched workgroup L runs on XCD L % 8, and the hardware hands workgroups
+// out in launch order as CUs free up.  XCD x owns the contiguous block of
+// lanes [x*hx, (x+1)*hx), so heads sharing a KV head (and its K/V tiles) share
+// that XCD's L2.  Inside the block the order is either query-tile-major with
+// the last query tiles (the heaviest under a causal mask) first, so the
+// in-order hand-out is a longest-first schedule (causal prefill, short
+// extends), or lane-major (a lane's tiles back to back, last first), which
+// keeps the workgroups of an XCD on fewer K/V streams when every tile costs
+// about the same (long non-causal work).  grid_pad = 8 * hx * n_qtiles.
+struct WorkItem {
+  int64_t lane;
+  int32_t qt;
+};
+__device__ __forceinline__ WorkItem work_item(const AttnArgs& a) {
   const int64_t L = blockIdx.x;
-  return (L & 7) * (a.grid_pad >> 3) + (L >> 3);
+  const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qtiles);
+  const int64_t j = L >> 3;
+  WorkItem w;
+  if (a.qt_major) {
+    w.qt = a.n_qtiles - 1 - (int32_t)(j / hx);
+    w.lane = (L & 7) * hx + j % hx;
+  } else {
+    w.qt = a.n_qtiles - 1 - (int32_t)(j % a.n_qtiles);
+    w.lane = (L & 7) * hx + j / a.n_qtiles;
+  }
+  return w;
+}
+static int64_t work_grid(int64_t lanes, int32_t n_qtiles) {
+  return 8 * ((lanes + 7) / 8) * (int64_t)n_qtiles;
 }
 
 struct KeySrc {
@@ -373,16 +399,15 @@ __device__ __forceinline__ int32_t context_len(const AttnArgs& a, int32_t seq) {
   return C < 0 ? 0 : C;
 }
 
-// Logical order: (seq, kv head, query head in group, query tile descending),
-// so heavy causal tiles start first and a KV head's tiles stay together.
+// Lanes: (seq, kv head, query head in group).
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const int64_t item = logical_item(a);
-  if (item >= a.items) return;
-  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
-  int64_t rest = item / a.n_qtiles;
+  const WorkItem w = work_item(a);
+  if (w.lane >= a.items) return;
+  const int32_t qt = w.qt;
+  int64_t rest = w.lane;
   const int32_t g = (int32_t)(rest % a.G);
   rest /= a.G;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
@@ -398,18 +423,18 @@ void prefill_kernel(AttnArgs a) {
   finish_rows<false>(a, h, s0, q0, qn, 0, S);
 }
 
-// Split extend.  Logical order: (seq, part, kv head, query head, query tile
-// descending).  Part 0: the new tokens among themselves (causal).  Part
+// Split extend.  Lanes: (seq, part, kv head, query head).  Part 0: the new
+// tokens among themselves (causal).  Part
 // p >= 1: the new tokens against context chunk p-1 = cached tokens
 // [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
 // fp32 partial; extend_merge_kernel combines them.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const int64_t item = logical_item(a);
-  if (item >= a.items) return;
-  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
-  int64_t rest = item / a.n_qtiles;
+  const WorkItem w = work_item(a);
+  if (w.lane >= a.items) return;
+  const int32_t qt = w.qt;
+  int64_t rest = w.lane;
   const int32_t g = (int32_t)(rest % a.G);
   rest /= a.G;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
@@ -446,10 +471,10 @@ void extend_kernel(AttnArgs a) {
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void extend_fused_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const int64_t item = logical_item(a);
-  if (item >= a.items) return;
-  const int32_t qt = a.n_qtiles - 1 - (int32_t)(item % a.n_qtiles);
-  int64_t rest = item / a.n_qtiles;
+  const WorkItem w = work_item(a);
+  if (w.lane >= a.items) return;
+  const int32_t qt = w.qt;
+  int64_t rest = w.lane;
   const int32_t g = (int32_t)(rest % a.G);
   rest /= a.G;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
@@ -532,8 +557,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.n_qtiles = (max_seqlen + kBM - 1) / kBM;
   a.n_parts = 1;
   a.qk_mult = scale * kLog2e;
-  a.items = (int64_t)num_seqs * num_q_heads * a.n_qtiles;
-  a.grid_pad = (a.items + 7) & ~(int64_t)7;
+  a.items = (int64_t)num_seqs * num_q_heads;             // lanes
+  a.grid_pad = work_grid(a.items, a.n_qtiles);
+  a.qt_major = causal ? 1 : 0;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
   if (causal)
     hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
@@ -605,15 +631,16 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.chunk_tokens = p.chunk_tokens;
   a.rows = total_new;
   a.qk_mult = scale * kLog2e;
+  a.qt_major = a.n_qtiles <= 16 ? 1 : 0;
   if (p.fused) {
-    a.items = (int64_t)num_seqs * num_q_heads * a.n_qtiles;
-    a.grid_pad = (a.items + 7) & ~(int64_t)7;
+    a.items = (int64_t)num_seqs * num_q_heads;           // lanes
+    a.grid_pad = work_grid(a.items, a.n_qtiles);
     if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(extend_fused_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  a.items = (int64_t)num_seqs * p.n_parts * num_q_heads * a.n_qtiles;
-  a.grid_pad = (a.items + 7) & ~(int64_t)7;
+  a.items = (int64_t)num_seqs * p.n_parts * num_q_heads;  // lanes
+  a.grid_pad = work_grid(a.items, a.n_qtiles);
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(extend_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
