@@ -16,8 +16,9 @@
 //
 // Tile core.  A workgroup of 4 waves owns 128 query rows of one query head
 // (32 rows per wave) and walks the key range in tiles of 64 keys staged in LDS
-// (double buffered: the next tile is loaded into registers while the current
-// one is consumed).  Per tile each wave computes
+// (double buffered: the next tile is moved from global memory straight into
+// the other LDS buffer by global_load_lds_dwordx4 while the current one is
+// consumed, with no staging registers).  Per tile each wave computes
 //     S^T (64 keys x 32 rows) = K Q^T         16 x v_mfma_f32_32x32x16_bf16
 //     online softmax per row in registers     (a row's 64 scores live in two
 //                                              lanes: in-lane max/sum + one
@@ -25,10 +26,11 @@
 //     O^T (128 dims x 32 rows) += V^T P^T      16 x v_mfma_f32_32x32x16_bf16
 // Q^T stays in registers as the B operand; K rows are read from LDS as the A
 // operand; V^T comes out of the natural row-major V tile through
-// ds_read_b64_tr_b16 (transposing LDS read); P^T is the S^T accumulator
-// converted to bf16 in place (its lane layout already is the B-operand layout
-// once the 16 keys of an MFMA k-step are taken in the order the accumulator
-// holds them).  Scores are kept in the exp2 domain (scale * log2 e folded in).
+// ds_read_b64_tr_b16 (transposing LDS read); rows are unpadded, their 16-byte
+// chunks permuted per row so both read patterns are free of bank conflicts;
+// P^T is the S^T accumulator converted to bf16 in place (its lane layout
+// already is the B-operand layout once the 16 keys of an MFMA k-step are taken
+// in the order the accumulator holds them).  Scores are kept in the exp2 domain (scale * log2 e folded in).
 //
 // Keys are read either from contiguous [tokens, H_kv, D] tensors (prefill, and
 // the new tokens of an extend) or straight from the paged NHD cache through
@@ -44,11 +46,10 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBM = 128;                   // query rows per workgroup
 constexpr int kBN = 64;                    // keys per tile
-constexpr int kKRow = 272;                 // LDS bytes per K row (256 + 16 pad)
-constexpr int kVRow = 320;                 // LDS bytes per V row (256 + 64 pad)
-constexpr int kKTile = kBN * kKRow;
-constexpr int kVTile = kBN * kVRow;
-constexpr int kStage = kKTile + kVTile;    // 37888 bytes
+constexpr int kRowB = 256;                 // LDS bytes per K or V row (unpadded)
+constexpr int kKTile = kBN * kRowB;
+constexpr int kVTile = kBN * kRowB;
+constexpr int kStage = kKTile + kVTile;    // 32768 bytes
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct AttnArgs {
@@ -124,57 +125,77 @@ __device__ __forceinline__ int64_t key_row_bytes(const AttnArgs& a, const KeySrc
   }
 }
 
-// Each thread stages rows tid/16 + 16*j (j = 0..3), 16-byte chunk tid%16, of
-// the K and V tiles; keys past k_end are clamped to the last key (finite data
-// whose probability is exactly zero).  Contiguous keys: kth / vth point at the
-// thread's first row of the first tile and advance by a constant per tile;
-// paged keys look their blocks up in the table.
+
+
+
+// Rows are stored unpadded with their 16-byte chunks permuted: K chunk c of
+// row r at position c ^ (r & 15) (the 32 rows of an MFMA operand read hit
+// distinct banks), V chunk c at c ^ 4(r & 3) (the transposed reads touch 4
+// rows x 4 chunks at a time).
+__device__ __forceinline__ int kswz(int row, int c) { return row * kRowB + ((c ^ (row & 15)) << 4); }
+__device__ __forceinline__ int vswz(int row, int c) { return row * kRowB + ((c ^ ((row & 3) << 2)) << 4); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
+}
+// 64 lanes' 16-byte global pieces into one contiguous 1 KB of LDS (lane i at
+// m0 + 16 i), with no staging registers.  Not known to the compiler: the
+// caller waits for them (vmcnt) before the barrier that publishes the stage.
+// m0 is a reserved register that the compiler sets right before each
+// instruction of its own that reads it, so overwriting it here is safe.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+}
+__device__ __forceinline__ void dma16s(uint32_t lds_base, uint32_t voff, const void* sbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory");
+}
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Tile starting at key k0 (keys past k_end clamped to the last key) into the
+// stage at `stage`: wave w moves rows 16w..16w+15 of K and of V.  Whole tiles
+// whose wave rows are contiguous in memory (contiguous keys, or one 16-token
+// block of the paged cache) use a uniform base and per-lane 32-bit offsets.
 template <bool PAGED>
-__device__ __forceinline__ void load_tile(const AttnArgs& a, const KeySrc& s, const uint8_t* kth,
-                                          const uint8_t* vth, int32_t k0, int32_t k_begin,
-                                          int32_t k_end, u32x4_t (&rk)[4], u32x4_t (&rv)[4]) {
-  const int c = threadIdx.x & 15;
-  if constexpr (!PAGED) {
+__device__ __forceinline__ void dma_tile(const AttnArgs& a, const KeySrc& s, uint8_t* stage,
+                                         int32_t k0, int32_t k_end) {
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int wave = wave_id();
+  const int pc = lane & 15;
+  const uint32_t kb = lds_addr(stage), vb = lds_addr(stage + kKTile);
+  const bool whole = PAGED ? (a.bs == 16 && (k0 & 15) == 0 && k0 + kBN <= k_end) : (k0 + kBN <= k_end);
+  if (whole) {
     const int64_t row_stride = (int64_t)a.Hkv * (kD * 2);
-    const int64_t toff = (int64_t)(k0 - k_begin) * row_stride;
-    const uint8_t* kb = kth + toff;
-    const uint8_t* vb = vth + toff;
-    if (k0 + kBN <= k_end) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rk[j] = *(const u32x4_t*)(kb + 16 * j * row_stride);
-        rv[j] = *(const u32x4_t*)(vb + 16 * j * row_stride);
-      }
+    int64_t tb;
+    if constexpr (PAGED) {
+      int32_t blk = __builtin_amdgcn_readfirstlane(s.trow[(k0 >> 4) + wave]);
+      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      tb = ((int64_t)blk * 16 - 16 * wave) * row_stride + s.hkv * (kD * 2);
     } else {
-      const int32_t r0 = k0 + (threadIdx.x >> 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int32_t key = r0 + 16 * j;
-        const int64_t d = (int64_t)((key < k_end ? key : k_end - 1) - r0) * row_stride;
-        rk[j] = *(const u32x4_t*)(kb + d);
-        rv[j] = *(const u32x4_t*)(vb + d);
-      }
+      tb = (int64_t)k0 * row_stride + s.hkv * (kD * 2);
     }
-  } else {
+    const uint8_t* kbase = s.kb + tb;
+    const uint8_t* vbase = s.vb + tb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int32_t key = k0 + (threadIdx.x >> 4) + 16 * j;
-      key = key < k_end ? key : k_end - 1;
-      const int64_t off = key_row_bytes<PAGED>(a, s, key) + c * 16;
-      rk[j] = *(const u32x4_t*)(s.kb + off);
-      rv[j] = *(const u32x4_t*)(s.vb + off);
+      const int row = 16 * wave + 4 * j + (lane >> 4);
+      const uint32_t ro = (uint32_t)(row * row_stride);
+      const uint32_t off = __builtin_amdgcn_readfirstlane((4 * wave + j) * 1024);
+      dma16s(kb + off, ro + ((pc ^ (row & 15)) << 4), kbase);
+      dma16s(vb + off, ro + ((pc ^ ((row & 3) << 2)) << 4), vbase);
     }
+    return;
   }
-}
-
-__device__ __forceinline__ void store_tile(uint8_t* stage, const u32x4_t (&rk)[4],
-                                           const u32x4_t (&rv)[4]) {
-  const int c = threadIdx.x & 15;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (threadIdx.x >> 4) + 16 * j;
-    *(u32x4_t*)(stage + row * kKRow + c * 16) = rk[j];
-    *(u32x4_t*)(stage + kKTile + row * kVRow + c * 16) = rv[j];
+    const int q = 4 * wave + j;
+    const int row = 4 * q + (lane >> 4);
+    int32_t key = k0 + row;
+    key = key < k_end ? key : k_end - 1;
+    const int64_t rb = key_row_bytes<PAGED>(a, s, key);
+    const uint32_t off = __builtin_amdgcn_readfirstlane(q * 1024);
+    dma16(kb + off, s.kb + rb + ((pc ^ (row & 15)) << 4));
+    dma16(vb + off, s.vb + rb + ((pc ^ ((row & 3) << 2)) << 4));
   }
 }
 
@@ -229,14 +250,9 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
   if (kend <= k_begin) return;               // uniform over the workgroup
   const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
 
-  const int64_t th_off = ((int64_t)(k_begin + (threadIdx.x >> 4)) * a.Hkv + src.hkv) * (kD * 2) +
-                         (threadIdx.x & 15) * 16;
-  const uint8_t* kth = src.kb + th_off;       // contiguous keys only
-  const uint8_t* vth = src.vb + th_off;
-  u32x4_t rk[4], rv[4];
   if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
-  load_tile<PAGED>(a, src, kth, vth, k_begin, k_begin, kend, rk, rv);
-  store_tile(smem, rk, rv);
+  dma_tile<PAGED>(a, src, smem, k_begin, kend);
+  dma_wait();
   __syncthreads();
 
   // One key tile.  MASK = false for tiles that no row of the workgroup needs
@@ -247,7 +263,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     const int32_t k0 = k_begin + t * kBN;
     uint8_t* st = smem + (t & 1) * kStage;
     const bool more = t + 1 < n_tiles;
-    if (more) load_tile<PAGED>(a, src, kth, vth, k0 + kBN, k_begin, kend, rk, rv);
+    if (more) dma_tile<PAGED>(a, src, smem + ((t + 1) & 1) * kStage, k0 + kBN, kend);
 
     // ---- S^T = K Q^T
     f32x16_t s[2];
@@ -255,9 +271,9 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
-      const uint8_t* kp = st + (32 * ks2 + r) * kKRow + 16 * hh;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s[ks2] = mfma32(*(const bf16x8_t*)(kp + 32 * ks), S.qb[ks], s[ks2]);
+      for (int ks = 0; ks < 8; ++ks)
+        s[ks2] = mfma32(*(const bf16x8_t*)(st + kswz(32 * ks2 + r, 2 * ks + hh)), S.qb[ks], s[ks2]);
     }
 
     // ---- mask, online softmax on raw scores (row = this lane's query row)
@@ -315,13 +331,13 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const int colb = (32 * dt + 16 * (g16 & 1) + 4 * (l16 & 3)) * 2;
-        const s16x4_t lo = lds_read_tr16(vt + vrow * kVRow + colb);
-        const s16x4_t hi = lds_read_tr16(vt + (vrow + 8) * kVRow + colb);
+        const s16x4_t lo = lds_read_tr16(vt + vswz(vrow, colb >> 4) + (colb & 15));
+        const s16x4_t hi = lds_read_tr16(vt + vswz(vrow + 8, colb >> 4) + (colb & 15));
         S.o[dt] = mfma32(cat_tr(lo, hi), pb[kk], S.o[dt]);
       }
     }
 
-    if (more) store_tile(smem + ((t + 1) & 1) * kStage, rk, rv);
+    dma_wait();
     __syncthreads();
   };
 
