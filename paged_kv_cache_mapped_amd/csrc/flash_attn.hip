@@ -258,12 +258,26 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
   // One key tile.  MASK = false for tiles that no row of the workgroup needs
   // masked (the whole tile is inside the key range and, for causal blocks,
   // below the diagonal of the first row); the mask code is not emitted there.
-  auto step = [&](int32_t t, auto mask_tag) {
+  // This lane's LDS byte offsets of its K fragments (k-step ks, rows r and
+  // r + 32 differ by a constant) and V^T fragments (dims 32 dt + ..; key
+  // steps and the +8 row half differ by constants), computed once.
+  uint32_t koff[8], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = kswz(r, 2 * ks + hh);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int colb = (32 * dt + 16 * (g16 & 1) + 4 * (l16 & 3)) * 2;
+    voff[dt] = kKTile + vswz(4 * (g16 >> 1) + (l16 >> 2), colb >> 4) + (colb & 15);
+  }
+
+  // One key tile in LDS buffer `par` (a compile-time 0/1 in the main loop,
+  // so buffer offsets fold into the LDS instructions' immediates).
+  auto step = [&](int32_t t, auto mask_tag, auto par) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int32_t k0 = k_begin + t * kBN;
-    uint8_t* st = smem + (t & 1) * kStage;
+    uint8_t* st = smem + par * kStage;
     const bool more = t + 1 < n_tiles;
-    if (more) dma_tile<PAGED>(a, src, smem + ((t + 1) & 1) * kStage, k0 + kBN, kend);
+    if (more) dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend);
 
     // ---- S^T = K Q^T
     f32x16_t s[2];
@@ -273,7 +287,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
       for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        s[ks2] = mfma32(*(const bf16x8_t*)(st + kswz(32 * ks2 + r, 2 * ks + hh)), S.qb[ks], s[ks2]);
+        s[ks2] = mfma32(*(const bf16x8_t*)(st + 8192 * ks2 + koff[ks]), S.qb[ks], s[ks2]);
     }
 
     // ---- mask, online softmax on raw scores (row = this lane's query row)
@@ -324,15 +338,12 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
       for (int j = 0; j < 8; ++j) pb[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
 
     // ---- O^T += V^T P^T
-    const uint8_t* vt = st + kKTile;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int vrow = 16 * kk + 4 * (g16 >> 1) + (l16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int colb = (32 * dt + 16 * (g16 & 1) + 4 * (l16 & 3)) * 2;
-        const s16x4_t lo = lds_read_tr16(vt + vswz(vrow, colb >> 4) + (colb & 15));
-        const s16x4_t hi = lds_read_tr16(vt + vswz(vrow + 8, colb >> 4) + (colb & 15));
+        const s16x4_t lo = lds_read_tr16(st + 4096 * kk + voff[dt]);
+        const s16x4_t hi = lds_read_tr16(st + 4096 * kk + 2048 + voff[dt]);
         S.o[dt] = mfma32(cat_tr(lo, hi), pb[kk], S.o[dt]);
       }
     }
@@ -347,9 +358,18 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     const int32_t tc = c >= 0 ? c / kBN + 1 : 0;
     t_plain = t_plain < tc ? t_plain : tc;
   }
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
   int32_t t = 0;
-  for (; t < t_plain; ++t) step(t, std::false_type{});
-  for (; t < n_tiles; ++t) step(t, std::true_type{});
+  for (; t + 1 < t_plain; t += 2) {
+    step(t, std::false_type{}, Par0{});
+    step(t + 1, std::false_type{}, Par1{});
+  }
+  if (t < t_plain) {                                      // t is even here
+    step(t, std::false_type{}, Par0{});
+    ++t;
+  }
+  for (; t < n_tiles; ++t) step(t, std::true_type{}, (int)(t & 1));
 }
 
 // Write the rows of this block: bf16 output + lse, or an fp32 partial
