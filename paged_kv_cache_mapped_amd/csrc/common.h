@@ -74,6 +74,26 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(u32x2_t w) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// (x of this lane, x of lane ^ 32), in some order, without an LDS round trip:
+// v_permlane32_swap issued directly (this compiler folds the two results of
+// __builtin_amdgcn_permlane32_swap(x, x, ...) into one); the nop covers a
+// VALU write of the inputs right before it.
+__device__ __forceinline__ void xor32_pair(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float a, b;
+  xor32_pair(x, a, b);
+  return a + b;
+}
+
 // Compiler-only barrier: keeps LDS stores and loads of one wave in program
 // order (the LDS itself processes one wave's requests in order).
 __device__ __forceinline__ void order_lds() { asm volatile("" ::: "memory"); }

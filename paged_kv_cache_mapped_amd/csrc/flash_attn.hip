@@ -30,7 +30,8 @@
 // chunks permuted per row so both read patterns are free of bank conflicts;
 // P^T is the S^T accumulator converted to bf16 in place (its lane layout
 // already is the B-operand layout once the 16 keys of an MFMA k-step are taken
-// in the order the accumulator holds them).  Scores are kept in the exp2 domain (scale * log2 e folded in).
+// in the order the accumulator holds them).  Scores are kept in the exp2
+// domain (scale * log2 e folded in).
 //
 // Keys are read either from contiguous [tokens, H_kv, D] tensors (prefill, and
 // the new tokens of an extend) or straight from the paged NHD cache through
@@ -307,7 +308,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * a.qk_mult;     // exp2 domain
+    mt = xor32_max(mt) * a.qk_mult;                     // exp2 domain
     // Lazy rescale: the reference max only moves when some row's max grew by
     // more than 8, so probabilities stay <= 2^8 and most tiles skip the O^T
     // rescale.  Any reference works: numerator and denominator share it.
@@ -380,7 +381,7 @@ __device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;
   const int32_t row = q0 + 32 * wave + r;
-  const float l_run = S.l_run + __shfl_xor(S.l_run, 32);
+  const float l_run = xor32_sum(S.l_run);
   if (row >= qn) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse_v = l_run > 0.f ? (S.m_run + __log2f(l_run)) * kLn2 : kNegInf;
