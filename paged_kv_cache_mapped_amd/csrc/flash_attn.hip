@@ -280,72 +280,78 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     const bool more = t + 1 < n_tiles;
     if (more) dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend);
 
-    // ---- S^T = K Q^T
-    f32x16_t s[2];
+    // A diagonal tile whose first key lies past every row of this wave
+    // contributes nothing to it: the wave only takes part in the copy and the
+    // barrier.
+    const bool skip = MASK && CAUSAL && k0 > q0 + 32 * wave + 31;
+    if (!skip) {
+      // ---- S^T = K Q^T
+      f32x16_t s[2];
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s[ks2] = mfma32(*(const bf16x8_t*)(st + 8192 * ks2 + koff[ks]), S.qb[ks], s[ks2]);
-    }
+        for (int ks = 0; ks < 8; ++ks)
+          s[ks2] = mfma32(*(const bf16x8_t*)(st + 8192 * ks2 + koff[ks]), S.qb[ks], s[ks2]);
+      }
 
-    // ---- mask, online softmax on raw scores (row = this lane's query row)
-    if constexpr (MASK) {
+      // ---- mask, online softmax on raw scores (row = this lane's query row)
+      if constexpr (MASK) {
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int32_t key = k0 + 32 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            bool dead = key >= kend;
+            if constexpr (CAUSAL) dead = dead || key > row;
+            if (dead) s[ks2][i] = kNegInf;
+          }
+      }
+      float mt = s[0][0];
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
+      mt = xor32_max(mt) * a.qk_mult;                     // exp2 domain
+      // Lazy rescale: the reference max only moves when some row's max grew by
+      // more than 8, so probabilities stay <= 2^8 and most tiles skip the O^T
+      // rescale.  Any reference works: numerator and denominator share it.
+      if (__builtin_amdgcn_ballot_w64(mt > S.m_run + 8.f) != 0) {
+        const float m_new = fmaxf(S.m_run, mt);
+        const float alpha = fast_exp2(S.m_run - (m_new == kNegInf ? 0.f : m_new));
+        S.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) S.o[dt] *= alpha;
+        S.m_run = m_new;
+      }
+      const float m_use = (S.m_run == kNegInf) ? 0.f : S.m_run;
+      float psum = 0.f;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int32_t key = k0 + 32 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          bool dead = key >= kend;
-          if constexpr (CAUSAL) dead = dead || key > row;
-          if (dead) s[ks2][i] = kNegInf;
+          s[ks2][i] = fast_exp2(__builtin_fmaf(s[ks2][i], a.qk_mult, -m_use));
+          psum += s[ks2][i];
         }
-    }
-    float mt = s[0][0];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
-    mt = xor32_max(mt) * a.qk_mult;                     // exp2 domain
-    // Lazy rescale: the reference max only moves when some row's max grew by
-    // more than 8, so probabilities stay <= 2^8 and most tiles skip the O^T
-    // rescale.  Any reference works: numerator and denominator share it.
-    if (__builtin_amdgcn_ballot_w64(mt > S.m_run + 8.f) != 0) {
-      const float m_new = fmaxf(S.m_run, mt);
-      const float alpha = fast_exp2(S.m_run - (m_new == kNegInf ? 0.f : m_new));
-      S.l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) S.o[dt] *= alpha;
-      S.m_run = m_new;
-    }
-    const float m_use = (S.m_run == kNegInf) ? 0.f : S.m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[ks2][i] = fast_exp2(__builtin_fmaf(s[ks2][i], a.qk_mult, -m_use));
-        psum += s[ks2][i];
-      }
-    S.l_run += psum;
+      S.l_run += psum;
 
-    // P^T as B operand: k-step kk covers keys 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}
-    bf16x8_t pb[4];
+      // P^T as B operand: k-step kk covers keys 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}
+      bf16x8_t pb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
+        for (int j = 0; j < 8; ++j) pb[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
 
-    // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const s16x4_t lo = lds_read_tr16(st + 4096 * kk + voff[dt]);
-        const s16x4_t hi = lds_read_tr16(st + 4096 * kk + 2048 + voff[dt]);
-        S.o[dt] = mfma32(cat_tr(lo, hi), pb[kk], S.o[dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const s16x4_t lo = lds_read_tr16(st + 4096 * kk + voff[dt]);
+          const s16x4_t hi = lds_read_tr16(st + 4096 * kk + 2048 + voff[dt]);
+          S.o[dt] = mfma32(cat_tr(lo, hi), pb[kk], S.o[dt]);
+        }
       }
     }
 
