@@ -191,7 +191,9 @@ int prefill_attn(const void* q, const void* k, const void* v,
  *   max_q_len / max_ctx_len   host-side bounds
  *   chunk_budget_tokens       context tokens per iteration across all
  *                 requests; each request's chunk = budget / num_seqs rounded
- *                 down to a multiple of block_size (at least one block)
+ *                 down to a multiple of max(block_size, 64), the key tile
+ *                 (at least one such unit).  The result does not depend on
+ *                 the chunk size beyond fp32 rounding.
  *   out           [total_new][num_q_heads][head_dim] bf16
  *   lse           [total_new][num_q_heads] fp32 or NULL
  *   workspace     >= extend_attn_workspace_bytes(...) bytes
