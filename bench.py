@@ -95,6 +95,56 @@ def counter_traffic(kernel, workload):
         return None
 
 
+class HipEvents:
+    """Timing events recorded straight through the HIP runtime that torch has
+    loaded, created with hipEventDisableSystemFence: a default event record
+    ends with a system-scope release (a writeback and invalidate of the GPU
+    caches), which costs several microseconds per marker and stalls the next
+    kernel.  The timestamps are taken the same way."""
+
+    FLAG = 0x20000000                     # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.events = []
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        self._ok(self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.ct.c_uint(self.FLAG)),
+                 "hipEventCreateWithFlags")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        self._ok(self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.ct.byref(out), a, b), "hipEventElapsedTime")
+        return float(out.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 # ----------------------------------------------------------------------------- workloads
 class Call:
     """One library call of the step with its algorithmic cost per launch."""
@@ -394,22 +444,22 @@ def main():
         # call of every timed step (events between every pair of calls would add
         # a marker packet each to the step)
         stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        hev = HipEvents()
+        ev = [(hev.new(), hev.new()) for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(args.steps):
             for c in calls:
                 if c.name == dominant:
-                    ev[s][0].record(stream)
+                    hev.record(ev[s][0], stream)
                     c.fn()
-                    ev[s][1].record(stream)
+                    hev.record(ev[s][1], stream)
                 else:
                     c.fn()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / max(args.steps, 1)
-        dom_ms = sum(a.elapsed_time(b) for a, b in ev) / max(len(ev), 1)
+        dom_ms = sum(hev.ms(a, b) for a, b in ev) / max(len(ev), 1)
 
         # every call's own duration, from events around it, after the timed region
         per = {}
@@ -417,14 +467,13 @@ def main():
             if c.name == dominant:
                 avg = dom_ms
             else:
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(args.steps)]
+                evs = [(hev.new(), hev.new()) for _ in range(args.steps)]
                 for a, b in evs:
-                    a.record(stream)
+                    hev.record(a, stream)
                     c.fn()
-                    b.record(stream)
+                    hev.record(b, stream)
                 torch.cuda.synchronize()
-                avg = sum(a.elapsed_time(b) for a, b in evs) / max(len(evs), 1)
+                avg = sum(hev.ms(a, b) for a, b in evs) / max(len(evs), 1)
             d = {"ms": round(avg, 5)}
             if c.bytes:
                 d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
@@ -462,6 +511,7 @@ def main():
             v, sample = cpu_sample()
             cpu = {"value": round(v, 4), "unit": unit, "cores": int(cores), "kind": "oracle",
                    "sample": sample}
+        hev.close()
         # free this workload's device memory before the next one
         del calls
         torch.cuda.synchronize()
