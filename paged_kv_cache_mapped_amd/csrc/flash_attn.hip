@@ -152,24 +152,54 @@ __device__ __forceinline__ void dma16s(uint32_t lds_base, uint32_t voff, const v
 }
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Whether the tile starting at k0 is one whose wave rows are contiguous in
+// memory: contiguous keys, or (paged) one 16-token block per wave.
+template <bool PAGED>
+__device__ __forceinline__ bool whole_tile(const AttnArgs& a, int32_t k0, int32_t k_end) {
+  return PAGED ? (a.bs == 16 && (k0 & 15) == 0 && k0 + kBN <= k_end) : (k0 + kBN <= k_end);
+}
+
+// The block-table entry of this wave's 16 rows of the whole paged tile at k0
+// (0 when the tile is not such a tile).  Looked up one tile ahead of the copy
+// that uses it: the value is first read by the next tile's copy, after the
+// current tile's wait, so neither the lookup nor the copy stalls.
+template <bool PAGED>
+__device__ __forceinline__ int32_t tile_block(const AttnArgs& a, const KeySrc& s, int32_t k0,
+                                              int32_t k_end) {
+  if constexpr (PAGED) {
+    return whole_tile<PAGED>(a, k0, k_end) ? s.trow[(k0 >> 4) + wave_id()] : 0;
+  } else {
+    return 0;
+  }
+}
+
+// Wait for this wave's copies, and tell the compiler that the look-ahead
+// lookup issued with them has landed too (it takes the value as an operand).
+// Without that, the compiler still counts the lookup as in flight and, before
+// the register is next written, waits on the vector-memory counter -- which
+// then also waits for the copy just issued for the following tile.
+__device__ __forceinline__ void dma_wait_for(int32_t& lookup) {
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(lookup)::"memory");
+}
+
 // Tile starting at key k0 (keys past k_end clamped to the last key) into the
 // stage at `stage`: wave w moves rows 16w..16w+15 of K and of V.  Whole tiles
 // whose wave rows are contiguous in memory (contiguous keys, or one 16-token
-// block of the paged cache) use a uniform base and per-lane 32-bit offsets.
+// block of the paged cache, `blk` its table entry from tile_block) use a
+// uniform base and per-lane 32-bit offsets.
 template <bool PAGED>
 __device__ __forceinline__ void dma_tile(const AttnArgs& a, const KeySrc& s, uint8_t* stage,
-                                         int32_t k0, int32_t k_end) {
+                                         int32_t k0, int32_t k_end, int32_t blk) {
   uint32_t lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int wave = wave_id();
   const int pc = lane & 15;
   const uint32_t kb = lds_addr(stage), vb = lds_addr(stage + kKTile);
-  const bool whole = PAGED ? (a.bs == 16 && (k0 & 15) == 0 && k0 + kBN <= k_end) : (k0 + kBN <= k_end);
-  if (whole) {
+  if (whole_tile<PAGED>(a, k0, k_end)) {
     const int64_t row_stride = (int64_t)a.Hkv * (kD * 2);
     int64_t tb;
     if constexpr (PAGED) {
-      int32_t blk = __builtin_amdgcn_readfirstlane(s.trow[(k0 >> 4) + wave]);
+      blk = __builtin_amdgcn_readfirstlane(blk);
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
       tb = ((int64_t)blk * 16 - 16 * wave) * row_stride + s.hkv * (kD * 2);
     } else {
@@ -252,8 +282,17 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
   const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
 
   if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
-  dma_tile<PAGED>(a, src, smem, k_begin, kend);
-  dma_wait();
+  dma_tile<PAGED>(a, src, smem, k_begin, kend, tile_block<PAGED>(a, src, k_begin, kend));
+  // table entry of the next tile's rows (the step copying tile t+1 looks up t+2)
+  int32_t blk_next = n_tiles > 1 ? tile_block<PAGED>(a, src, k_begin + kBN, kend) : 0;
+  dma_wait_for(blk_next);
+  // Q^T was loaded before this wait; passing it through an empty asm tells the
+  // compiler so.  Otherwise its wait insertion treats the Q loads as possibly
+  // outstanding at the loop head and waits on the vector-memory counter before
+  // the first MFMA of every tile -- which also waits for the next tile's copy
+  // issued just before, and serialises the double buffer.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(S.qb[ks]));
   __syncthreads();
 
   // One key tile.  MASK = false for tiles that no row of the workgroup needs
@@ -278,7 +317,10 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     const int32_t k0 = k_begin + t * kBN;
     uint8_t* st = smem + par * kStage;
     const bool more = t + 1 < n_tiles;
-    if (more) dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend);
+    if (more) {
+      dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend, blk_next);
+      if (t + 2 < n_tiles) blk_next = tile_block<PAGED>(a, src, k0 + 2 * kBN, kend);
+    }
 
     // A diagonal tile whose first key lies past every row of this wave
     // contributes nothing to it: the wave only takes part in the copy and the
@@ -355,7 +397,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
       }
     }
 
-    dma_wait();
+    dma_wait_for(blk_next);
     __syncthreads();
   };
 
