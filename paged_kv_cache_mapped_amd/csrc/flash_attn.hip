@@ -14,11 +14,13 @@
 //   and an LSE merge, (3) a final merge.  Each chunk yields an output and an
 //   LSE that records its softmax denominator.
 //
-// Tile core.  A workgroup of 4 waves owns 128 query rows of one query head
-// (32 rows per wave) and walks the key range in tiles of 64 keys staged in LDS
-// (double buffered: the next tile is moved from global memory straight into
-// the other LDS buffer by global_load_lds_dwordx4 while the current one is
-// consumed, with no staging registers).  Per tile each wave computes
+// Tile core.  A workgroup of 8 waves owns two blocks of 128 query rows that
+// read the same keys -- two query heads of one KV head, or two consecutive
+// query tiles of one head -- 32 rows per wave, and walks the key range in
+// tiles of 64 keys staged in LDS (double buffered: the next tile is moved from
+// global memory straight into the other LDS buffer by global_load_lds_dwordx4
+// while the current one is consumed, with no staging registers).  Each tile
+// copied serves 256 query rows.  Per tile each wave computes
 //     S^T (64 keys x 32 rows) = K Q^T         16 x v_mfma_f32_32x32x16_bf16
 //     online softmax per row in registers     (a row's 64 scores live in two
 //                                              lanes: in-lane max/sum + one
@@ -45,7 +47,9 @@ namespace pkv {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kBM = 128;                   // query rows per workgroup
+constexpr int kBM = 128;                   // query rows per row block
+constexpr int kWaves = 8;                  // two row blocks of 4 waves
+constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;                    // keys per tile
 constexpr int kRowB = 256;                 // LDS bytes per K or V row (unpadded)
 constexpr int kKTile = kBN * kRowB;
@@ -67,15 +71,23 @@ struct AttnArgs {
   float* part_o;            // [n_parts][rows][Hq][D]
   float* part_lse;          // [n_parts][rows][Hq]
   int32_t max_blocks, num_blocks, bs, bs_log2;
-  int32_t Hq, Hkv, G, num_seqs, n_qtiles, n_parts, chunk_tokens, rows;
-  int64_t items;            // lanes (work items = lanes x query tiles)
+  int32_t Hq, Hkv, G, num_seqs, n_parts, chunk_tokens, rows;
+  int32_t pairs;            // 1: a work item is two query heads of one KV head over the
+                            // same 128 rows; 0: two consecutive 128-row tiles of one head
+  int32_t Gs;               // lanes per KV head: G / 2 (pairs) or G
+  int32_t n_qitems;         // query items per lane: 128-row tiles (pairs) or tile pairs
+  int64_t items;            // lanes (work items = lanes x query items)
   int64_t grid_pad;         // launched workgroups (multiple of 8)
   int32_t qt_major;         // work order inside an XCD's block of lanes
   float qk_mult;            // scale * log2(e)
 };
 
-// Work order.  A work item is (lane, query tile), lanes being the
-// (sequence[, part], KV head, query head) combinations in that order.
+// Work order.  A work item is (lane, query item), lanes being the
+// (sequence[, part], KV head, query-head pair or query head) combinations in
+// that order.  A workgroup of 8 waves runs two 128-row blocks that share every
+// K/V tile it copies into LDS: two query heads of one KV head over the same
+// rows when the group size is even, else two consecutive query tiles of one
+// head.
 // Launched workgroup L runs on XCD L % 8, and the hardware hands workgroups
 // out in launch order as CUs free up.  XCD x owns the contiguous block of
 // lanes [x*hx, (x+1)*hx), so heads sharing a KV head (and its K/V tiles) share
@@ -84,27 +96,50 @@ struct AttnArgs {
 // in-order hand-out is a longest-first schedule (causal prefill, short
 // extends), or lane-major (a lane's tiles back to back, last first), which
 // keeps the workgroups of an XCD on fewer K/V streams when every tile costs
-// about the same (long non-causal work).  grid_pad = 8 * hx * n_qtiles.
+// about the same (long non-causal work).  grid_pad = 8 * hx * n_qitems.
 struct WorkItem {
   int64_t lane;
-  int32_t qt;
+  int32_t qi;
 };
 __device__ __forceinline__ WorkItem work_item(const AttnArgs& a) {
   const int64_t L = blockIdx.x;
-  const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qtiles);
+  const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qitems);
   const int64_t j = L >> 3;
   WorkItem w;
   if (a.qt_major) {
-    w.qt = a.n_qtiles - 1 - (int32_t)(j / hx);
+    w.qi = a.n_qitems - 1 - (int32_t)(j / hx);
     w.lane = (L & 7) * hx + j % hx;
   } else {
-    w.qt = a.n_qtiles - 1 - (int32_t)(j % a.n_qtiles);
-    w.lane = (L & 7) * hx + j / a.n_qtiles;
+    w.qi = a.n_qitems - 1 - (int32_t)(j % a.n_qitems);
+    w.lane = (L & 7) * hx + j / a.n_qitems;
   }
   return w;
 }
-static int64_t work_grid(int64_t lanes, int32_t n_qtiles) {
-  return 8 * ((lanes + 7) / 8) * (int64_t)n_qtiles;
+static int64_t work_grid(int64_t lanes, int32_t n_qitems) {
+  return 8 * ((lanes + 7) / 8) * (int64_t)n_qitems;
+}
+
+// This wave's row block of work item (KV head hkv, lane-in-group gsel, query
+// item qi): waves 0-3 take block 0, waves 4-7 block 1.  q0 is the block's
+// first row; q0_lo / q0_hi the first rows of the workgroup's first / last
+// block (they bound the keys the workgroup needs under a causal mask).
+struct RowBlock {
+  int32_t h, q0, q0_lo, q0_hi;
+};
+__device__ __forceinline__ RowBlock row_block(const AttnArgs& a, int32_t hkv, int32_t gsel,
+                                              int32_t qi) {
+  const int rb = wave_id() >> 2;
+  RowBlock r;
+  if (a.pairs) {
+    r.h = hkv * a.G + 2 * gsel + rb;
+    r.q0 = r.q0_lo = r.q0_hi = qi * kBM;
+  } else {
+    r.h = hkv * a.G + gsel;
+    r.q0_lo = 2 * qi * kBM;
+    r.q0_hi = r.q0_lo + kBM;
+    r.q0 = r.q0_lo + rb * kBM;
+  }
+  return r;
 }
 
 struct KeySrc {
@@ -159,7 +194,7 @@ __device__ __forceinline__ bool whole_tile(const AttnArgs& a, int32_t k0, int32_
   return PAGED ? (a.bs == 16 && (k0 & 15) == 0 && k0 + kBN <= k_end) : (k0 + kBN <= k_end);
 }
 
-// The block-table entry of this wave's 16 rows of the whole paged tile at k0
+// The block-table entry of this wave's 8 rows of the whole paged tile at k0
 // (0 when the tile is not such a tile).  Looked up one tile ahead of the copy
 // that uses it: the value is first read by the next tile's copy, after the
 // current tile's wait, so neither the lookup nor the copy stalls.
@@ -167,7 +202,7 @@ template <bool PAGED>
 __device__ __forceinline__ int32_t tile_block(const AttnArgs& a, const KeySrc& s, int32_t k0,
                                               int32_t k_end) {
   if constexpr (PAGED) {
-    return whole_tile<PAGED>(a, k0, k_end) ? s.trow[(k0 >> 4) + wave_id()] : 0;
+    return whole_tile<PAGED>(a, k0, k_end) ? s.trow[(k0 >> 4) + (wave_id() >> 1)] : 0;
   } else {
     return 0;
   }
@@ -183,10 +218,10 @@ __device__ __forceinline__ void dma_wait_for(int32_t& lookup) {
 }
 
 // Tile starting at key k0 (keys past k_end clamped to the last key) into the
-// stage at `stage`: wave w moves rows 16w..16w+15 of K and of V.  Whole tiles
-// whose wave rows are contiguous in memory (contiguous keys, or one 16-token
-// block of the paged cache, `blk` its table entry from tile_block) use a
-// uniform base and per-lane 32-bit offsets.
+// stage at `stage`: wave w moves rows 8w..8w+7 of K and of V.  Whole tiles
+// whose wave rows are contiguous in memory (contiguous keys, or half of one
+// 16-token block of the paged cache, `blk` its table entry from tile_block)
+// use a uniform base and per-lane 32-bit offsets.
 template <bool PAGED>
 __device__ __forceinline__ void dma_tile(const AttnArgs& a, const KeySrc& s, uint8_t* stage,
                                          int32_t k0, int32_t k_end, int32_t blk) {
@@ -201,25 +236,25 @@ __device__ __forceinline__ void dma_tile(const AttnArgs& a, const KeySrc& s, uin
     if constexpr (PAGED) {
       blk = __builtin_amdgcn_readfirstlane(blk);
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-      tb = ((int64_t)blk * 16 - 16 * wave) * row_stride + s.hkv * (kD * 2);
+      tb = ((int64_t)blk * 16 - 16 * (wave >> 1)) * row_stride + s.hkv * (kD * 2);
     } else {
       tb = (int64_t)k0 * row_stride + s.hkv * (kD * 2);
     }
     const uint8_t* kbase = s.kb + tb;
     const uint8_t* vbase = s.vb + tb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * wave + 4 * j + (lane >> 4);
+    for (int j = 0; j < 2; ++j) {
+      const int row = 8 * wave + 4 * j + (lane >> 4);
       const uint32_t ro = (uint32_t)(row * row_stride);
-      const uint32_t off = __builtin_amdgcn_readfirstlane((4 * wave + j) * 1024);
+      const uint32_t off = __builtin_amdgcn_readfirstlane((2 * wave + j) * 1024);
       dma16s(kb + off, ro + ((pc ^ (row & 15)) << 4), kbase);
       dma16s(vb + off, ro + ((pc ^ ((row & 3) << 2)) << 4), vbase);
     }
     return;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = 4 * wave + j;
+  for (int j = 0; j < 2; ++j) {
+    const int q = 2 * wave + j;
     const int row = 4 * q + (lane >> 4);
     int32_t key = k0 + row;
     key = key < k_end ? key : k_end - 1;
@@ -244,7 +279,7 @@ __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t 
                                           int32_t qn, RowState& S) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;
-  const int32_t row = q0 + 32 * wave + r;
+  const int32_t row = q0 + 32 * (wave & 3) + r;
   // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
   const bf16x8_t zero = {};
   const __bf16* qp = a.q + ((qbase + row) * a.Hq + h) * kD + 8 * hh;
@@ -258,24 +293,25 @@ __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t 
   S.l_run = 0.f;
 }
 
-// Fold keys [k_begin, k_end) of one source into the running state.  CAUSAL:
-// key j is visible to row i iff j <= i (keys and rows indexed within the
-// sequence).  The LDS double buffer is filled and drained inside, so phases
-// with different sources can follow each other.
+// Fold keys [k_begin, k_end) of one source into the running state of this
+// wave's rows (block starting at q0; the workgroup's blocks start at q0_lo and
+// q0_hi).  CAUSAL: key j is visible to row i iff j <= i (keys and rows indexed
+// within the sequence).  The LDS double buffer is filled and drained inside,
+// so phases with different sources can follow each other.
 template <bool PAGED, bool CAUSAL, bool FIRST = false>
 __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
-                                         int32_t q0, int32_t qn, int32_t k_begin, int32_t k_end,
-                                         RowState& S) {
+                                         int32_t q0, int32_t q0_lo, int32_t q0_hi, int32_t qn,
+                                         int32_t k_begin, int32_t k_end, RowState& S) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
-  const int32_t row = q0 + 32 * wave + r;       // this lane's query row (in sequence)
+  const int32_t row = q0 + 32 * (wave & 3) + r; // this lane's query row (in sequence)
 
   // key range actually needed by this block
   int32_t kend = k_end;
   if constexpr (CAUSAL) {
-    const int32_t last_row = min(q0 + kBM, qn) - 1;
+    const int32_t last_row = min(q0_hi + kBM, qn) - 1;
     kend = min(kend, last_row + 1);
   }
   if (kend <= k_begin) return;               // uniform over the workgroup
@@ -325,7 +361,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     // A diagonal tile whose first key lies past every row of this wave
     // contributes nothing to it: the wave only takes part in the copy and the
     // barrier.
-    const bool skip = MASK && CAUSAL && k0 > q0 + 32 * wave + 31;
+    const bool skip = MASK && CAUSAL && k0 > q0 + 32 * (wave & 3) + 31;
     if (!skip) {
       // ---- S^T = K Q^T
       f32x16_t s[2];
@@ -403,7 +439,7 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 
   int32_t t_plain = (kend - k_begin) / kBN;             // tiles fully inside the key range
   if constexpr (CAUSAL) {
-    const int32_t c = q0 - k_begin - (kBN - 1);          // last key of tile <= first row
+    const int32_t c = q0_lo - k_begin - (kBN - 1);       // last key of tile <= first row
     const int32_t tc = c >= 0 ? c / kBN + 1 : 0;
     t_plain = t_plain < tc ? t_plain : tc;
   }
@@ -428,7 +464,7 @@ __device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_
                                             int32_t q0, int32_t qn, int32_t part, RowState& S) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;
-  const int32_t row = q0 + 32 * wave + r;
+  const int32_t row = q0 + 32 * (wave & 3) + r;
   const float l_run = xor32_sum(S.l_run);
   if (row >= qn) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -484,99 +520,97 @@ __device__ __forceinline__ int32_t context_len(const AttnArgs& a, int32_t seq) {
   return C < 0 ? 0 : C;
 }
 
-// Lanes: (seq, kv head, query head in group).
+// Lanes: (seq, kv head, query-head pair or query head).
 template <bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
   const WorkItem w = work_item(a);
   if (w.lane >= a.items) return;
-  const int32_t qt = w.qt;
   int64_t rest = w.lane;
-  const int32_t g = (int32_t)(rest % a.G);
-  rest /= a.G;
+  const int32_t gsel = (int32_t)(rest % a.Gs);
+  rest /= a.Gs;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
   const int32_t seq = (int32_t)(rest / a.Hkv);
   const int32_t s0 = a.cu[seq];
   const int32_t qn = a.cu[seq + 1] - s0;
-  const int32_t q0 = qt * kBM;
-  if (q0 >= qn) return;
-  const int32_t h = hkv * a.G + g;
+  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+  if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   RowState S;
-  init_rows(a, h, s0, q0, qn, S);
-  run_keys<false, CAUSAL, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
-  finish_rows<false>(a, h, s0, q0, qn, 0, S);
+  init_rows(a, rb.h, s0, rb.q0, qn, S);
+  run_keys<false, CAUSAL, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
+                                qn, 0, qn, S);
+  finish_rows<false>(a, rb.h, s0, rb.q0, qn, 0, S);
 }
 
-// Split extend.  Lanes: (seq, part, kv head, query head).  Part 0: the new
+// Split extend.  Lanes: (seq, part, kv head, query-head pair or query head).  Part 0: the new
 // tokens among themselves (causal).  Part
 // p >= 1: the new tokens against context chunk p-1 = cached tokens
 // [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
 // fp32 partial; extend_merge_kernel combines them.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
   const WorkItem w = work_item(a);
   if (w.lane >= a.items) return;
-  const int32_t qt = w.qt;
   int64_t rest = w.lane;
-  const int32_t g = (int32_t)(rest % a.G);
-  rest /= a.G;
+  const int32_t gsel = (int32_t)(rest % a.Gs);
+  rest /= a.Gs;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
   rest /= a.Hkv;
   const int32_t part = (int32_t)(rest % a.n_parts);
   const int32_t seq = (int32_t)(rest / a.n_parts);
   const int32_t s0 = a.cu[seq];
   const int32_t qn = a.cu[seq + 1] - s0;
-  const int32_t q0 = qt * kBM;
-  if (q0 >= qn) return;
-  const int32_t h = hkv * a.G + g;
+  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+  if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   RowState S;
   if (part == 0) {
-    init_rows(a, h, s0, q0, qn, S);
-    run_keys<false, true, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
+    init_rows(a, rb.h, s0, rb.q0, qn, S);
+    run_keys<false, true, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
+                                qn, 0, qn, S);
   } else {
     const int32_t C = context_len(a, seq);
     const int32_t kb = (part - 1) * a.chunk_tokens;
     if (kb >= C) return;
-    init_rows(a, h, s0, q0, qn, S);
-    run_keys<true, false, true>(a, smem, paged_keys(a, seq, hkv), q0, qn, kb,
+    init_rows(a, rb.h, s0, rb.q0, qn, S);
+    run_keys<true, false, true>(a, smem, paged_keys(a, seq, hkv), rb.q0, rb.q0_lo, rb.q0_hi, qn, kb,
                                 min(C, kb + a.chunk_tokens), S);
   }
-  finish_rows<true>(a, h, s0, q0, qn, part, S);
+  finish_rows<true>(a, rb.h, s0, rb.q0, qn, part, S);
 }
 
 // Fused extend, used when the batch has enough query tiles to fill the GPU
 // without splitting along the context.  Logical order: (seq, kv head, query
-// head, query tile descending).  One workgroup runs every context chunk of
+// head pair or head, query item descending).  One workgroup runs every context chunk of
 // its rows in order and then the new tokens, carrying one running softmax
 // state: the LSE merge of each chunk into the running output is done in
 // registers (rescaling by the exponential of the max difference), so no
 // partials are written and no merge pass is needed.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_fused_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
   const WorkItem w = work_item(a);
   if (w.lane >= a.items) return;
-  const int32_t qt = w.qt;
   int64_t rest = w.lane;
-  const int32_t g = (int32_t)(rest % a.G);
-  rest /= a.G;
+  const int32_t gsel = (int32_t)(rest % a.Gs);
+  rest /= a.Gs;
   const int32_t hkv = (int32_t)(rest % a.Hkv);
   const int32_t seq = (int32_t)(rest / a.Hkv);
   const int32_t s0 = a.cu[seq];
   const int32_t qn = a.cu[seq + 1] - s0;
-  const int32_t q0 = qt * kBM;
-  if (q0 >= qn) return;
-  const int32_t h = hkv * a.G + g;
+  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+  if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   const int32_t C = context_len(a, seq);
   RowState S;
-  init_rows(a, h, s0, q0, qn, S);
+  init_rows(a, rb.h, s0, rb.q0, qn, S);
   const KeySrc ctx = paged_keys(a, seq, hkv);
   for (int32_t kb = 0; kb < C; kb += a.chunk_tokens)
-    run_keys<true, false>(a, smem, ctx, q0, qn, kb, min(C, kb + a.chunk_tokens), S);
-  run_keys<false, true>(a, smem, contiguous_keys(a, s0, hkv), q0, qn, 0, qn, S);
-  finish_rows<false>(a, h, s0, q0, qn, 0, S);
+    run_keys<true, false>(a, smem, ctx, rb.q0, rb.q0_lo, rb.q0_hi, qn, kb,
+                          min(C, kb + a.chunk_tokens), S);
+  run_keys<false, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi, qn, 0, qn,
+                        S);
+  finish_rows<false>(a, rb.h, s0, rb.q0, qn, 0, S);
 }
 
 // Final merge of the extend parts of each (row, head), one wave each:
@@ -624,6 +658,14 @@ int32_t log2i(int32_t v) {
 
 }  // namespace
 
+// Row blocks of a work item: two query heads of one KV head when the group
+// size is even, else two consecutive query tiles of one head.
+static void set_pairing(AttnArgs& a, int32_t n_qtiles) {
+  a.pairs = (a.G % 2 == 0) ? 1 : 0;
+  a.Gs = a.pairs ? a.G / 2 : a.G;
+  a.n_qitems = a.pairs ? n_qtiles : (n_qtiles + 1) / 2;
+}
+
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                           int32_t num_seqs, int32_t max_seqlen, int32_t num_q_heads,
                           int32_t num_kv_heads, float scale, int32_t causal, void* out, float* lse,
@@ -639,17 +681,18 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.Hkv = num_kv_heads;
   a.G = num_q_heads / num_kv_heads;
   a.num_seqs = num_seqs;
-  a.n_qtiles = (max_seqlen + kBM - 1) / kBM;
+  const int32_t n_qtiles = (max_seqlen + kBM - 1) / kBM;
+  set_pairing(a, n_qtiles);
   a.n_parts = 1;
   a.qk_mult = scale * kLog2e;
-  a.items = (int64_t)num_seqs * num_q_heads;             // lanes
-  a.grid_pad = work_grid(a.items, a.n_qtiles);
+  a.items = (int64_t)num_seqs * num_kv_heads * a.Gs;     // lanes
+  a.grid_pad = work_grid(a.items, a.n_qitems);
   a.qt_major = causal ? 1 : 0;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
   if (causal)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -711,23 +754,24 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.Hkv = c.num_kv_heads;
   a.G = num_q_heads / c.num_kv_heads;
   a.num_seqs = num_seqs;
-  a.n_qtiles = (max_q_len + kBM - 1) / kBM;
+  const int32_t n_qtiles = (max_q_len + kBM - 1) / kBM;
+  set_pairing(a, n_qtiles);
   a.n_parts = p.n_parts;
   a.chunk_tokens = p.chunk_tokens;
   a.rows = total_new;
   a.qk_mult = scale * kLog2e;
-  a.qt_major = a.n_qtiles <= 16 ? 1 : 0;
+  a.qt_major = n_qtiles <= 16 ? 1 : 0;
   if (p.fused) {
-    a.items = (int64_t)num_seqs * num_q_heads;           // lanes
-    a.grid_pad = work_grid(a.items, a.n_qtiles);
+    a.items = (int64_t)num_seqs * a.Hkv * a.Gs;          // lanes
+    a.grid_pad = work_grid(a.items, a.n_qitems);
     if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(extend_fused_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(extend_fused_kernel, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  a.items = (int64_t)num_seqs * p.n_parts * num_q_heads;  // lanes
-  a.grid_pad = work_grid(a.items, a.n_qtiles);
+  a.items = (int64_t)num_seqs * p.n_parts * a.Hkv * a.Gs;  // lanes
+  a.grid_pad = work_grid(a.items, a.n_qitems);
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(extend_kernel, dim3((unsigned)a.grid_pad), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(extend_kernel, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rh = (int64_t)total_new * num_q_heads;
