@@ -38,6 +38,12 @@
 // Keys are read either from contiguous [tokens, H_kv, D] tensors (prefill, and
 // the new tokens of an extend) or straight from the paged NHD cache through
 // the block table (extend context chunks) -- no gather copy.
+//
+// Prefill runs persistent: one workgroup per CU walks a fixed serpentine
+// list of work items and, during the last key tile of each, copies the next
+// item's Q rows and first K/V tile into LDS, so consecutive items follow each
+// other without a start-up wait; outputs leave through LDS as whole rows.
+// The extend kernels are launched one workgroup per work item.
 #include <type_traits>
 
 #include "common.h"
@@ -101,8 +107,8 @@ struct WorkItem {
   int64_t lane;
   int32_t qi;
 };
-__device__ __forceinline__ WorkItem work_item(const AttnArgs& a) {
-  const int64_t L = blockIdx.x;
+template <class Args>
+__device__ __forceinline__ WorkItem work_item(const Args& a, int64_t L) {
   const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qitems);
   const int64_t j = L >> 3;
   WorkItem w;
@@ -118,6 +124,21 @@ __device__ __forceinline__ WorkItem work_item(const AttnArgs& a) {
 static int64_t work_grid(int64_t lanes, int32_t n_qitems) {
   return 8 * ((lanes + 7) / 8) * (int64_t)n_qitems;
 }
+// Persistent walk: the launched grid holds one workgroup per CU (a multiple of
+// 8); launched workgroup b runs the virtual workgroups 8m + (b & 7) of its
+// XCD, m = r J + j in even rounds r and r J + J - 1 - j in odd ones (j = b / 8,
+// J = workgroups per XCD): a serpentine over the heaviest-first order.
+// Returns -1 past the end.
+template <class Args>
+__device__ __forceinline__ int64_t virtual_wg(const Args& a, int32_t r) {
+  const int32_t J = gridDim.x >> 3, j = blockIdx.x >> 3;
+  const int64_t m = (int64_t)r * J + ((r & 1) ? J - 1 - j : j);
+  return m < (a.grid_pad >> 3) ? 8 * m + (blockIdx.x & 7) : -1;
+}
+static unsigned persistent_grid(int64_t grid_pad) {
+  const int64_t slots = 8 * (int64_t)(device_cu_count() / 8);
+  return (unsigned)(grid_pad < slots ? grid_pad : slots);
+}
 
 // This wave's row block of work item (KV head hkv, lane-in-group gsel, query
 // item qi): waves 0-3 take block 0, waves 4-7 block 1.  q0 is the block's
@@ -126,7 +147,8 @@ static int64_t work_grid(int64_t lanes, int32_t n_qitems) {
 struct RowBlock {
   int32_t h, q0, q0_lo, q0_hi;
 };
-__device__ __forceinline__ RowBlock row_block(const AttnArgs& a, int32_t hkv, int32_t gsel,
+template <class Args>
+__device__ __forceinline__ RowBlock row_block(const Args& a, int32_t hkv, int32_t gsel,
                                               int32_t qi) {
   const int rb = wave_id() >> 2;
   RowBlock r;
@@ -149,8 +171,8 @@ struct KeySrc {
   int32_t hkv;
 };
 
-template <bool PAGED>
-__device__ __forceinline__ int64_t key_row_bytes(const AttnArgs& a, const KeySrc& s, int32_t key) {
+template <bool PAGED, class Args>
+__device__ __forceinline__ int64_t key_row_bytes(const Args& a, const KeySrc& s, int32_t key) {
   if constexpr (PAGED) {
     int32_t blk = s.trow[key >> a.bs_log2];
     blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
@@ -173,6 +195,15 @@ __device__ __forceinline__ int vswz(int row, int c) { return row * kRowB + ((c ^
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint8_t*)p);
 }
+// The lane index through an asm the compiler cannot move, so that per-lane
+// address arithmetic at item boundaries is not hoisted out of the item loop
+// (it would hold registers during the whole key loop).
+__device__ __forceinline__ int lane_here() {
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return (int)lane;
+}
+
 // 64 lanes' 16-byte global pieces into one contiguous 1 KB of LDS (lane i at
 // m0 + 16 i), with no staging registers.  Not known to the compiler: the
 // caller waits for them (vmcnt) before the barrier that publishes the stage.
@@ -189,8 +220,8 @@ __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" :
 
 // Whether the tile starting at k0 is one whose wave rows are contiguous in
 // memory: contiguous keys, or (paged) one 16-token block per wave.
-template <bool PAGED>
-__device__ __forceinline__ bool whole_tile(const AttnArgs& a, int32_t k0, int32_t k_end) {
+template <bool PAGED, class Args>
+__device__ __forceinline__ bool whole_tile(const Args& a, int32_t k0, int32_t k_end) {
   return PAGED ? (a.bs == 16 && (k0 & 15) == 0 && k0 + kBN <= k_end) : (k0 + kBN <= k_end);
 }
 
@@ -198,8 +229,8 @@ __device__ __forceinline__ bool whole_tile(const AttnArgs& a, int32_t k0, int32_
 // (0 when the tile is not such a tile).  Looked up one tile ahead of the copy
 // that uses it: the value is first read by the next tile's copy, after the
 // current tile's wait, so neither the lookup nor the copy stalls.
-template <bool PAGED>
-__device__ __forceinline__ int32_t tile_block(const AttnArgs& a, const KeySrc& s, int32_t k0,
+template <bool PAGED, class Args>
+__device__ __forceinline__ int32_t tile_block(const Args& a, const KeySrc& s, int32_t k0,
                                               int32_t k_end) {
   if constexpr (PAGED) {
     return whole_tile<PAGED>(a, k0, k_end) ? s.trow[(k0 >> 4) + (wave_id() >> 1)] : 0;
@@ -222,8 +253,8 @@ __device__ __forceinline__ void dma_wait_for(int32_t& lookup) {
 // whose wave rows are contiguous in memory (contiguous keys, or half of one
 // 16-token block of the paged cache, `blk` its table entry from tile_block)
 // use a uniform base and per-lane 32-bit offsets.
-template <bool PAGED>
-__device__ __forceinline__ void dma_tile(const AttnArgs& a, const KeySrc& s, uint8_t* stage,
+template <bool PAGED, class Args>
+__device__ __forceinline__ void dma_tile(const Args& a, const KeySrc& s, uint8_t* stage,
                                          int32_t k0, int32_t k_end, int32_t blk) {
   uint32_t lane;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
@@ -293,43 +324,28 @@ __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t 
   S.l_run = 0.f;
 }
 
-// Fold keys [k_begin, k_end) of one source into the running state of this
-// wave's rows (block starting at q0; the workgroup's blocks start at q0_lo and
-// q0_hi).  CAUSAL: key j is visible to row i iff j <= i (keys and rows indexed
-// within the sequence).  The LDS double buffer is filled and drained inside,
-// so phases with different sources can follow each other.
-template <bool PAGED, bool CAUSAL, bool FIRST = false>
-__device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
-                                         int32_t q0, int32_t q0_lo, int32_t q0_hi, int32_t qn,
-                                         int32_t k_begin, int32_t k_end, RowState& S) {
-  const int lane = threadIdx.x & 63;
+// The tile loop folding keys [k_begin, kend) (n_tiles tiles of kBN) into the
+// running state of this wave's rows (block starting at q0; the workgroup's
+// first block starts at q0_lo).  CAUSAL: key j is visible to row i iff j <= i
+// (keys and rows indexed within the sequence).  On entry the first tile is in
+// LDS buffer SB, published by a barrier, and blk_next holds the table entry
+// of the second one (paged keys).  Tile t is in buffer (t + SB) & 1; each step
+// copies the next tile into the other buffer.  hooks.last(buffer) runs at the
+// start of the last tile, when the other buffer is free: a persistent
+// workgroup copies its next work item's first tile there.
+struct NoHooks {
+  __device__ __forceinline__ void last(uint8_t*) const {}
+};
+template <bool PAGED, bool CAUSAL, int SB, class Hooks, class Args>
+__device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const KeySrc& src,
+                                         int32_t q0, int32_t q0_lo, int32_t k_begin, int32_t kend,
+                                         int32_t n_tiles, int32_t blk_next, RowState& S,
+                                         const Hooks& hooks) {
+  const int lane = lane_here();
   const int wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
   const int32_t row = q0 + 32 * (wave & 3) + r; // this lane's query row (in sequence)
-
-  // key range actually needed by this block
-  int32_t kend = k_end;
-  if constexpr (CAUSAL) {
-    const int32_t last_row = min(q0_hi + kBM, qn) - 1;
-    kend = min(kend, last_row + 1);
-  }
-  if (kend <= k_begin) return;               // uniform over the workgroup
-  const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
-
-  if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
-  dma_tile<PAGED>(a, src, smem, k_begin, kend, tile_block<PAGED>(a, src, k_begin, kend));
-  // table entry of the next tile's rows (the step copying tile t+1 looks up t+2)
-  int32_t blk_next = n_tiles > 1 ? tile_block<PAGED>(a, src, k_begin + kBN, kend) : 0;
-  dma_wait_for(blk_next);
-  // Q^T was loaded before this wait; passing it through an empty asm tells the
-  // compiler so.  Otherwise its wait insertion treats the Q loads as possibly
-  // outstanding at the loop head and waits on the vector-memory counter before
-  // the first MFMA of every tile -- which also waits for the next tile's copy
-  // issued just before, and serialises the double buffer.
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(S.qb[ks]));
-  __syncthreads();
 
   // One key tile.  MASK = false for tiles that no row of the workgroup needs
   // masked (the whole tile is inside the key range and, for causal blocks,
@@ -348,12 +364,12 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 
   // One key tile in LDS buffer `par` (a compile-time 0/1 in the main loop,
   // so buffer offsets fold into the LDS instructions' immediates).
-  auto step = [&](int32_t t, auto mask_tag, auto par) {
+  auto step = [&](int32_t t, auto mask_tag, auto par, auto last_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool LAST = decltype(last_tag)::value;
     const int32_t k0 = k_begin + t * kBN;
     uint8_t* st = smem + par * kStage;
-    const bool more = t + 1 < n_tiles;
-    if (more) {
+    if constexpr (!LAST) {
       dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend, blk_next);
       if (t + 2 < n_tiles) blk_next = tile_block<PAGED>(a, src, k0 + 2 * kBN, kend);
     }
@@ -376,15 +392,15 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 
       // ---- mask, online softmax on raw scores (row = this lane's query row)
       if constexpr (MASK) {
+        // score (ks2, i) is key k0 + 4 hh + e, e = 32 ks2 + 8 (i / 4) + i % 4; it is
+        // dead past the key range and, causal, past this lane's row
+        int32_t lim = kend - 1 - (k0 + 4 * hh);
+        if constexpr (CAUSAL) lim = min(lim, row - (k0 + 4 * hh));
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int32_t key = k0 + 32 * ks2 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            bool dead = key >= kend;
-            if constexpr (CAUSAL) dead = dead || key > row;
-            if (dead) s[ks2][i] = kNegInf;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (32 * ks2 + 8 * (i >> 2) + (i & 3) > lim) s[ks2][i] = kNegInf;
       }
       float mt = s[0][0];
 #pragma unroll
@@ -443,18 +459,72 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
     const int32_t tc = c >= 0 ? c / kBN + 1 : 0;
     t_plain = t_plain < tc ? t_plain : tc;
   }
-  using Par0 = std::integral_constant<int, 0>;
-  using Par1 = std::integral_constant<int, 1>;
+  // tile t sits in buffer (t + SB) & 1
+  using Par0 = std::integral_constant<int, SB>;
+  using Par1 = std::integral_constant<int, 1 - SB>;
+  using No = std::false_type;
+  using Yes = std::true_type;
+  const int32_t n_body = n_tiles - 1;                   // tiles followed by another one
+  const int32_t tp = t_plain < n_body ? t_plain : n_body;
   int32_t t = 0;
-  for (; t + 1 < t_plain; t += 2) {
-    step(t, std::false_type{}, Par0{});
-    step(t + 1, std::false_type{}, Par1{});
+  for (; t + 1 < tp; t += 2) {
+    step(t, No{}, Par0{}, No{});
+    step(t + 1, No{}, Par1{}, No{});
   }
-  if (t < t_plain) {                                      // t is even here
-    step(t, std::false_type{}, Par0{});
+  if (t < tp) {                                           // t is even here
+    step(t, No{}, Par0{}, No{});
     ++t;
   }
-  for (; t < n_tiles; ++t) step(t, std::true_type{}, (int)(t & 1));
+  for (; t < n_body; ++t) step(t, Yes{}, (int)((t + SB) & 1), No{});
+  // the last tile: the other buffer is free from here on
+  const int par_last = (t + SB) & 1;
+  hooks.last(smem + (1 - par_last) * kStage);
+  __builtin_amdgcn_sched_barrier(0);    // keep the hook's code apart from the tile's
+  // (buffer offsets as compile-time constants: with a run-time buffer the
+  // compiler builds every LDS address in a register of its own)
+  if (t < t_plain) {
+    if (par_last == SB) step(t, No{}, Par0{}, Yes{});
+    else step(t, No{}, Par1{}, Yes{});
+  } else {
+    if (par_last == SB) step(t, Yes{}, Par0{}, Yes{});
+    else step(t, Yes{}, Par1{}, Yes{});
+  }
+}
+
+
+// Fold keys [k_begin, k_end) of one source into the running state of this
+// wave's rows (block starting at q0; the workgroup's blocks start at q0_lo and
+// q0_hi): copy the first tile, then the tile loop.  The LDS double buffer is
+// filled and drained inside, so phases with different sources can follow
+// each other.
+template <bool PAGED, bool CAUSAL, bool FIRST = false>
+__device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
+                                         int32_t q0, int32_t q0_lo, int32_t q0_hi, int32_t qn,
+                                         int32_t k_begin, int32_t k_end, RowState& S) {
+  // key range actually needed by this block
+  int32_t kend = k_end;
+  if constexpr (CAUSAL) {
+    const int32_t last_row = min(q0_hi + kBM, qn) - 1;
+    kend = min(kend, last_row + 1);
+  }
+  if (kend <= k_begin) return;               // uniform over the workgroup
+  const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
+
+  if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
+  dma_tile<PAGED>(a, src, smem, k_begin, kend, tile_block<PAGED>(a, src, k_begin, kend));
+  // table entry of the next tile's rows (the step copying tile t+1 looks up t+2)
+  int32_t blk_next = n_tiles > 1 ? tile_block<PAGED>(a, src, k_begin + kBN, kend) : 0;
+  dma_wait_for(blk_next);
+  // Q^T was loaded before this wait; passing it through an empty asm tells the
+  // compiler so.  Otherwise its wait insertion treats the Q loads as possibly
+  // outstanding at the loop head and waits on the vector-memory counter before
+  // the first MFMA of every tile -- which also waits for the next tile's copy
+  // issued just before, and serialises the double buffer.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(S.qb[ks]));
+  __syncthreads();
+  key_loop<PAGED, CAUSAL, 0>(a, smem, src, q0, q0_lo, k_begin, kend, n_tiles, blk_next, S,
+                            NoHooks{});
 }
 
 // Write the rows of this block: bf16 output + lse, or an fp32 partial
@@ -495,7 +565,8 @@ __device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_
   }
 }
 
-__device__ __forceinline__ KeySrc contiguous_keys(const AttnArgs& a, int32_t s0, int32_t hkv) {
+template <class Args>
+__device__ __forceinline__ KeySrc contiguous_keys(const Args& a, int32_t s0, int32_t hkv) {
   KeySrc src;
   src.kb = (const uint8_t*)(a.k + (int64_t)s0 * a.Hkv * kD);
   src.vb = (const uint8_t*)(a.v + (int64_t)s0 * a.Hkv * kD);
@@ -504,7 +575,8 @@ __device__ __forceinline__ KeySrc contiguous_keys(const AttnArgs& a, int32_t s0,
   return src;
 }
 
-__device__ __forceinline__ KeySrc paged_keys(const AttnArgs& a, int32_t seq, int32_t hkv) {
+template <class Args>
+__device__ __forceinline__ KeySrc paged_keys(const Args& a, int32_t seq, int32_t hkv) {
   KeySrc src;
   src.kb = a.kc;
   src.vb = a.vc;
@@ -513,34 +585,233 @@ __device__ __forceinline__ KeySrc paged_keys(const AttnArgs& a, int32_t seq, int
   return src;
 }
 
-__device__ __forceinline__ int32_t context_len(const AttnArgs& a, int32_t seq) {
+template <class Args>
+__device__ __forceinline__ int32_t context_len(const Args& a, int32_t seq) {
   int32_t C = a.ctx_lens[seq];
   const int32_t cap = a.max_blocks << a.bs_log2;
   C = C > cap ? cap : C;
   return C < 0 ? 0 : C;
 }
 
-// Lanes: (seq, kv head, query-head pair or query head).
+// ---- Streamed prefill: one persistent workgroup per CU runs its work items
+// back to back.  During the last key tile of an item it decodes the next item,
+// copies that item's first K/V tile into the free LDS buffer, and each wave
+// copies its next 32 query rows into its own 8 KB region of a Q area, so an
+// item starts with nothing to wait for.  The output of an item is staged
+// through the same region (after the next Q has been read from it) and
+// written as whole 256-byte rows.
+constexpr int kQRegion = 32 * kRowB;                     // one wave's 32 query rows
+constexpr int kQArea = 2 * kStage;                       // Q / output area
+constexpr int kSlotArea = kQArea + kWaves * kQRegion;    // per wave: the next item (64 bytes)
+constexpr int kStreamSmem = kSlotArea + kWaves * 64;
+
+struct StreamItem {
+  int32_t valid, h, q0w, q0_lo, qn, s0, hkv, kend, n_tiles;
+};
+constexpr int kItemWords = 9;
+
+// The kernel argument block as a constant-memory pointer the compiler cannot
+// see through: fields read through it are loaded where they are used
+// (scalar loads) instead of being hoisted to the kernel entry and held in
+// registers across the whole item loop.
+typedef const __attribute__((address_space(4))) AttnArgs* ArgsPtr;
+__device__ __forceinline__ ArgsPtr args_here() {
+  // the kernels take the argument block as their only argument, at offset 0
+  ArgsPtr p = (ArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+// Next valid work item of this workgroup's walk, from round r on (this
+// wave's rows: q0w is its first row; keys [0, kend) in n_tiles tiles).
+template <bool CAUSAL>
+__device__ __forceinline__ StreamItem next_item(int32_t& r) {
+  const auto& a = *args_here();
+  StreamItem it = {};
+  for (;; ++r) {
+    const int64_t L = virtual_wg(a, r);
+    if (L < 0) return it;
+    const WorkItem w = work_item(a, L);
+    if (w.lane >= a.items) continue;
+    int64_t rest = w.lane;
+    const int32_t gsel = (int32_t)(rest % a.Gs);
+    rest /= a.Gs;
+    const int32_t hkv = (int32_t)(rest % a.Hkv);
+    const int32_t seq = (int32_t)(rest / a.Hkv);
+    const int32_t s0 = a.cu[seq];
+    const int32_t qn = a.cu[seq + 1] - s0;
+    const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+    if (rb.q0_lo >= qn) continue;
+    it.valid = 1;
+    it.h = uniform(rb.h);
+    it.q0w = uniform(rb.q0 + 32 * (wave_id() & 3));
+    it.q0_lo = uniform(rb.q0_lo);
+    it.qn = uniform(qn);
+    it.s0 = uniform(s0);
+    it.hkv = uniform(hkv);
+    it.kend = uniform(CAUSAL ? min(rb.q0_hi + kBM, qn) : qn);
+    it.n_tiles = uniform((it.kend + kBN - 1) / kBN);
+    ++r;
+    return it;
+  }
+}
+
+// The item through this wave's LDS slot (lane i < kItemWords holds word i).
+__device__ __forceinline__ void put_item(uint8_t* smem, const StreamItem& it) {
+  const int lane = lane_here();
+  const int32_t w[kItemWords] = {it.valid, it.h,    it.q0w,    it.q0_lo, it.qn,
+                                 it.s0,    it.hkv,  it.kend,   it.n_tiles};
+  int32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < kItemWords; ++i) v = lane == i ? w[i] : v;
+  if (lane < kItemWords) ((int32_t*)(smem + kSlotArea + wave_id() * 64))[lane] = v;
+}
+__device__ __forceinline__ StreamItem get_item(const uint8_t* smem) {
+  const int32_t* p = (const int32_t*)(smem + kSlotArea + wave_id() * 64);
+  const int lane = lane_here();
+  const int32_t v = lane < kItemWords ? p[lane] : 0;
+  StreamItem it;
+  it.valid = __builtin_amdgcn_readlane(v, 0);
+  it.h = __builtin_amdgcn_readlane(v, 1);
+  it.q0w = __builtin_amdgcn_readlane(v, 2);
+  it.q0_lo = __builtin_amdgcn_readlane(v, 3);
+  it.qn = __builtin_amdgcn_readlane(v, 4);
+  it.s0 = __builtin_amdgcn_readlane(v, 5);
+  it.hkv = __builtin_amdgcn_readlane(v, 6);
+  it.kend = __builtin_amdgcn_readlane(v, 7);
+  it.n_tiles = __builtin_amdgcn_readlane(v, 8);
+  return it;
+}
+
+// This wave's 32 query rows of `it` into its Q region: row i at 256 i, its
+// 16-byte chunk c at position c ^ (i & 15) (rows past the sequence repeat its
+// last row; their results are never stored).
+template <class Args>
+__device__ __forceinline__ void dma_q(const Args& a, uint8_t* smem, const StreamItem& it) {
+  const int lane = lane_here();
+  const int wave = wave_id();
+  const uint32_t base = lds_addr(smem + kQArea + wave * kQRegion);
+  const int pc = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rw = 4 * j + (lane >> 4);
+    int32_t row = it.q0w + rw;
+    row = row < it.qn ? row : it.qn - 1;
+    const uint8_t* g = (const uint8_t*)a.q + ((int64_t)(it.s0 + row) * a.Hq + it.h) * (kD * 2) +
+                       ((pc ^ (rw & 15)) << 4);
+    dma16(base + __builtin_amdgcn_readfirstlane(j * 1024), g);
+  }
+}
+
+__device__ __forceinline__ void read_q(const uint8_t* smem, RowState& S) {
+  const int lane = lane_here(), r = lane & 31, hh = lane >> 5;
+  const uint8_t* reg = smem + kQArea + wave_id() * kQRegion;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) S.qb[ks] = *(const bf16x8_t*)(reg + kswz(r, 2 * ks + hh));
+}
+
+__device__ __forceinline__ void clear_rows(RowState& S) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S.o[dt][i] = 0.f;
+  S.m_run = kNegInf;
+  S.l_run = 0.f;
+}
+
+// Output rows (bf16) and lse of this wave's rows q0w.. of head h, staged
+// through its Q region so that every store writes whole rows.
+template <class Args>
+__device__ __forceinline__ void store_rows(const Args& a, uint8_t* smem, int32_t h, int32_t s0,
+                                           int32_t q0w, int32_t qn, RowState& S) {
+  const int lane = lane_here(), r = lane & 31, hh = lane >> 5;
+  uint8_t* reg = smem + kQArea + wave_id() * kQRegion;
+  const float l_run = xor32_sum(S.l_run);
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const bf16x4_t v4 = {(__bf16)(S.o[dt][4 * i4] * inv), (__bf16)(S.o[dt][4 * i4 + 1] * inv),
+                           (__bf16)(S.o[dt][4 * i4 + 2] * inv), (__bf16)(S.o[dt][4 * i4 + 3] * inv)};
+      *(bf16x4_t*)(reg + kswz(r, 4 * dt + i4) + 8 * hh) = v4;
+    }
+  if (hh == 0 && q0w + r < qn && a.lse) {
+    const float lse_v = l_run > 0.f ? (S.m_run + __log2f(l_run)) * kLn2 : kNegInf;
+    a.lse[(int64_t)(s0 + q0w + r) * a.Hq + h] = lse_v;
+  }
+  order_lds();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rw = 4 * j + (lane >> 4), c = lane & 15;
+    const bf16x8_t v = *(const bf16x8_t*)(reg + kswz(rw, c));
+    const int32_t row = q0w + rw;
+    if (row < qn) *(bf16x8_t*)(a.out + ((int64_t)(s0 + row) * a.Hq + h) * kD + 8 * c) = v;
+  }
+}
+
+// Copies that start item n: its Q rows and its first key tile (into buf).
+template <class Args>
+__device__ __forceinline__ void start_item(const Args& a, uint8_t* smem, uint8_t* buf,
+                                           const StreamItem& n) {
+  dma_q(a, smem, n);
+  dma_tile<false>(a, contiguous_keys(a, n.s0, n.hkv), buf, 0, n.kend, 0);
+}
+
+// Hooks of an item's key loop: at its last tile, decode the next item, leave
+// it in the slot and start its copies.
+template <bool CAUSAL>
+struct NextItem {
+  ArgsPtr a;
+  uint8_t* smem;
+  int32_t* r;
+  __device__ __forceinline__ void last(uint8_t* buf) const {
+    const StreamItem n = next_item<CAUSAL>(*r);
+    put_item(smem, n);
+    if (n.valid) start_item(*a, smem, buf, n);
+  }
+};
+
+// Prefill as a stream of work items per persistent workgroup.
 template <bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
-void prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const WorkItem w = work_item(a);
-  if (w.lane >= a.items) return;
-  int64_t rest = w.lane;
-  const int32_t gsel = (int32_t)(rest % a.Gs);
-  rest /= a.Gs;
-  const int32_t hkv = (int32_t)(rest % a.Hkv);
-  const int32_t seq = (int32_t)(rest / a.Hkv);
-  const int32_t s0 = a.cu[seq];
-  const int32_t qn = a.cu[seq + 1] - s0;
-  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
-  if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
+void prefill_stream_kernel(AttnArgs) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStreamSmem];
+  int32_t r = 0;
+  StreamItem cur = next_item<CAUSAL>(r);
+  if (!cur.valid) return;
+  start_item(*args_here(), smem, smem, cur);
+  dma_wait();
+  __syncthreads();
   RowState S;
-  init_rows(a, rb.h, s0, rb.q0, qn, S);
-  run_keys<false, CAUSAL, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
-                                qn, 0, qn, S);
-  finish_rows<false>(a, rb.h, s0, rb.q0, qn, 0, S);
+  read_q(smem, S);
+  clear_rows(S);
+  int32_t sb = 0;                                   // LDS buffer of the item's first tile
+  for (;;) {
+    {
+      const ArgsPtr A = args_here();
+      const NextItem<CAUSAL> hooks = {A, smem, &r};
+      const KeySrc src = contiguous_keys(*A, cur.s0, cur.hkv);
+      const int32_t q0 = cur.q0w - 32 * (wave_id() & 3);
+      if (sb == 0)
+        key_loop<false, CAUSAL, 0>(*A, smem, src, q0, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0, S,
+                                   hooks);
+      else
+        key_loop<false, CAUSAL, 1>(*A, smem, src, q0, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0, S,
+                                   hooks);
+    }
+    sb = (sb + cur.n_tiles) & 1;
+    // The last tile's barrier has passed: the next item's Q and first tile are in LDS.
+    const StreamItem nxt = get_item(smem);
+    RowState N;
+    if (nxt.valid) read_q(smem, N);
+    store_rows(*args_here(), smem, cur.h, cur.s0, cur.q0w, cur.qn, S);
+    if (!nxt.valid) break;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) S.qb[ks] = N.qb[ks];
+    clear_rows(S);
+    cur = nxt;
+  }
 }
 
 // Split extend.  Lanes: (seq, part, kv head, query-head pair or query head).  Part 0: the new
@@ -551,7 +822,7 @@ void prefill_kernel(AttnArgs a) {
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const WorkItem w = work_item(a);
+  const WorkItem w = work_item(a, blockIdx.x);
   if (w.lane >= a.items) return;
   int64_t rest = w.lane;
   const int32_t gsel = (int32_t)(rest % a.Gs);
@@ -590,7 +861,7 @@ void extend_kernel(AttnArgs a) {
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_fused_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const WorkItem w = work_item(a);
+  const WorkItem w = work_item(a, blockIdx.x);
   if (w.lane >= a.items) return;
   int64_t rest = w.lane;
   const int32_t gsel = (int32_t)(rest % a.Gs);
@@ -689,10 +960,11 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.grid_pad = work_grid(a.items, a.n_qitems);
   a.qt_major = causal ? 1 : 0;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(persistent_grid(a.grid_pad));
   if (causal)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(prefill_stream_kernel<true>, grid, dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(prefill_stream_kernel<false>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
