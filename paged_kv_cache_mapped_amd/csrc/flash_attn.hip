@@ -853,14 +853,19 @@ void extend_kernel(AttnArgs a) {
 
 // Fused extend, used when the batch has enough query tiles to fill the GPU
 // without splitting along the context.  Logical order: (seq, kv head, query
-// head pair or head, query item descending).  One workgroup runs every context chunk of
-// its rows in order and then the new tokens, carrying one running softmax
-// state: the LSE merge of each chunk into the running output is done in
+// head pair or head, query item descending).  One workgroup runs the cached
+// context of its rows and then the new tokens, carrying one running softmax
+// state: the LSE merge of the context into the running output is done in
 // registers (rescaling by the exponential of the max difference), so no
-// partials are written and no merge pass is needed.
+// partials are written and no merge pass is needed.  The context is walked as
+// one key range: its 64-key tiles are the ones a walk chunk by chunk would
+// take (chunk lengths are whole tiles), in the same order, so the result is
+// the same, without a pipeline restart per chunk.  Q comes in through the
+// per-wave LDS regions and the output leaves through them, as in the
+// persistent prefill.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_fused_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQArea + kWaves * kQRegion];
   const WorkItem w = work_item(a, blockIdx.x);
   if (w.lane >= a.items) return;
   int64_t rest = w.lane;
@@ -873,15 +878,37 @@ void extend_fused_kernel(AttnArgs a) {
   const RowBlock rb = row_block(a, hkv, gsel, w.qi);
   if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   const int32_t C = context_len(a, seq);
-  RowState S;
-  init_rows(a, rb.h, s0, rb.q0, qn, S);
+  StreamItem it = {};
+  it.valid = 1;
+  it.h = rb.h;
+  it.q0w = rb.q0 + 32 * (wave_id() & 3);
+  it.qn = qn;
+  it.s0 = s0;
+  const int32_t kend = min(rb.q0_hi + kBM, qn);          // new tokens, causal
   const KeySrc ctx = paged_keys(a, seq, hkv);
-  for (int32_t kb = 0; kb < C; kb += a.chunk_tokens)
-    run_keys<true, false>(a, smem, ctx, rb.q0, rb.q0_lo, rb.q0_hi, qn, kb,
-                          min(C, kb + a.chunk_tokens), S);
-  run_keys<false, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi, qn, 0, qn,
-                        S);
-  finish_rows<false>(a, rb.h, s0, rb.q0, qn, 0, S);
+  const KeySrc fresh = contiguous_keys(a, s0, hkv);
+  dma_q(a, smem, it);
+  int32_t blk1 = 0;
+  if (C > 0) {
+    dma_tile<true>(a, ctx, smem, 0, C, tile_block<true>(a, ctx, 0, C));
+    blk1 = C > kBN ? tile_block<true>(a, ctx, kBN, C) : 0;
+  } else {
+    dma_tile<false>(a, fresh, smem, 0, kend, 0);
+  }
+  dma_wait_for(blk1);
+  __syncthreads();
+  RowState S;
+  read_q(smem, S);
+  clear_rows(S);
+  if (C > 0) {
+    const int32_t nt = (C + kBN - 1) / kBN;
+    key_loop<true, false, 0>(a, smem, ctx, rb.q0, rb.q0_lo, 0, C, nt, blk1, S, NoHooks{});
+    run_keys<false, true>(a, smem, fresh, rb.q0, rb.q0_lo, rb.q0_hi, qn, 0, qn, S);
+  } else {
+    const int32_t nt_new = (kend + kBN - 1) / kBN;
+    key_loop<false, true, 0>(a, smem, fresh, rb.q0, rb.q0_lo, 0, kend, nt_new, 0, S, NoHooks{});
+  }
+  store_rows(a, smem, rb.h, s0, it.q0w, qn, S);
 }
 
 // Final merge of the extend parts of each (row, head), one wave each:
