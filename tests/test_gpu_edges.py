@@ -134,3 +134,27 @@ def test_extend_one_new_token_equals_decode():
     torch().cuda.synchronize()
     assert max_err(bf16_to_f64(do), out) <= 2 * BF16_TOL
     assert max_err(dl.cpu().numpy().astype(np.float64), lse) <= LSE_TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 1), (6, 2)])
+def test_prefill_persistent_walk(causal, Hq, Hkv):
+    """Many more work items than CUs, so every persistent workgroup runs a
+    series of them, with odd and even key-tile counts (an item then starts in
+    either LDS buffer) and many skipped items (query tiles past a short
+    sequence); head groups of 8 (two heads per item) and of 3 (two query tiles
+    per item).  Sampled rows of every sequence against the oracle."""
+    rng = np.random.default_rng(46)
+    lens = [int(x) for x in rng.integers(1, 320, 300)] + [130, 129, 65, 64, 63, 1]
+    say(f"prefill persistent walk causal={causal} {Hq}:{Hkv} seqs={len(lens)}")
+    cu, q, k, v, out, lse = _prefill(lens, Hq, Hkv, causal, 47)
+    rows = []
+    for n in range(len(lens)):
+        s0, L = int(cu[n]), lens[n]
+        rows += sorted({s0, s0 + L - 1, s0 + int(rng.integers(0, L))})
+    ro, rl = oa.prefill(ob.to_f64(q), ob.to_f64(k), ob.to_f64(v), cu, SCALE, causal, rows=rows)
+    e = max_err(out[rows], ro[rows])
+    el = max_err(lse[rows], rl[rows])
+    say(f"  max|err| out {e:.3e} lse {el:.3e} over {len(rows)} rows")
+    assert e <= BF16_TOL and el <= LSE_TOL
+    assert not np.isnan(out).any()
