@@ -158,3 +158,38 @@ def test_prefill_persistent_walk(causal, Hq, Hkv):
     say(f"  max|err| out {e:.3e} lse {el:.3e} over {len(rows)} rows")
     assert e <= BF16_TOL and el <= LSE_TOL
     assert not np.isnan(out).any()
+
+
+@pytest.mark.parametrize("bs", [1, 16, 32])
+def test_extend_fused_ragged_contexts(bs):
+    """Enough query tiles for the fused extend (64 heads x 17 query tiles),
+    with cached contexts of 1, 63, 64, 65 and 1000 tokens (partial first and
+    last key tiles) and block sizes whose tiles are not whole blocks (1, 32)
+    as well as 16; the cache past every context is poisoned.  Sampled rows
+    of every request against the oracle."""
+    ctx, new = [1, 63, 64, 65, 1000], [600, 500, 400, 300, 300]
+    nb = sum((c + n + bs - 1) // bs for c, n in zip(ctx, new)) + 64
+    mb = w.mixed_batch(48, 64, 4, 128, bs, nb, [], ctx, new, [])
+    w.poison_cache(mb.cache, mb.ext_tables, mb.ext_ctx)
+    say(f"extend fused ragged contexts bs={bs} ctx={ctx} new={new}")
+    e0, e1 = mb.rows_extend
+    dc = device_cache(mb.cache)
+    q, kn, vn = dev(mb.q[e0:e1]), dev(mb.k_new[e0:e1]), dev(mb.v_new[e0:e1])
+    out, lse = pk.extend_attn(dc, q, kn, vn, dev(mb.ext_cu_q), dev(mb.ext_ctx), dev(mb.ext_tables),
+                              max(new), max(ctx), mb.scale, 32768)
+    torch().cuda.synchronize()
+    out, lse = bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(49)
+    rows = []
+    for i in range(len(new)):
+        s0 = int(mb.ext_cu_q[i])
+        rows += sorted({s0, s0 + 1, s0 + 127, s0 + 128, s0 + new[i] - 1}
+                       | {s0 + int(x) for x in rng.integers(0, new[i], 6)})
+    ro, rl = oa.extend(ob.to_f64(mb.q[e0:e1]), ob.to_f64(mb.k_new[e0:e1]),
+                       ob.to_f64(mb.v_new[e0:e1]), mb.ext_cu_q, mb.ext_ctx,
+                       oracle_cache(mb.cache), mb.ext_tables, mb.scale, rows=rows)
+    e = max_err(out[rows], ro[rows])
+    el = max_err(lse[rows], rl[rows])
+    say(f"  max|err| out {e:.3e} lse {el:.3e} over {len(rows)} rows")
+    assert e <= BF16_TOL and el <= LSE_TOL
+    assert not np.isnan(out).any()
