@@ -121,18 +121,25 @@ int kv_write(const kv_cache_t* cache, const void* k, const void* v,
  * cache, so it is bound by memory bandwidth.
  *   q             [batch][num_q_heads][head_dim] bf16
  *   block_tables  [batch][max_blocks_per_seq] int32 physical block ids
- *   seq_lens      [batch] int32, 1 <= seq_lens[b] <= max_seq_len (device)
+ *   seq_lens      [batch] int32, 0 <= seq_lens[b] <= max_seq_len (device)
  *   max_seq_len   host-side upper bound of seq_lens (sizes the split grid)
  *   out           [batch][num_q_heads][head_dim] bf16
  *   lse           [batch][num_q_heads] fp32 or NULL
- *   workspace     >= paged_decode_workspace_bytes(...) bytes, 16-byte aligned
+ *   scale         softmax scale, finite and > 0 (else KV_EINVAL)
+ *   workspace     >= paged_decode_workspace_bytes(...) bytes, 16-byte aligned;
+ *                 holds the plan and the fp32 partials of split requests
+ *                 (about (pieces + batch) * num_q_heads * 516 bytes; a few
+ *                 MB to tens of MB at serving shapes), contents need not be
+ *                 initialised and are overwritten by every call
  * Balanced split-K: the requests' token streams are concatenated and cut into
  * equal pieces (a small on-device planning pass reads seq_lens), so every
  * workgroup reads the same amount of KV; requests spanning several pieces are
  * combined by log-sum-exp weights ([ROCm] section "Processing details of the
  * three paths", LSE merge).  Lengths above max_seq_len or the table capacity
- * are clamped; a request of length 0 leaves its output unwritten;
- * batch * max_seq_len must stay below 2^31.
+ * are clamped; a request of length 0 sees no key and gets out = 0 and
+ * lse = -inf; batch * max_seq_len must stay below 2^31.  The workspace query
+ * sizes for the current device; a call whose stream belongs to a device with
+ * more compute units may need more (KV_ENOSPC says so).
  * Layouts/dtypes: NHD bf16, NHD fp8, PRESHUFFLED bf16, PRESHUFFLED fp8.
  * num_q_heads must be a multiple of num_kv_heads.
  * ------------------------------------------------------------------------- */
@@ -168,6 +175,7 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch,
  *                 sequence n owns rows cu_seqlens[n] .. cu_seqlens[n+1]-1
  *   max_seqlen    host-side upper bound of the sequence lengths
  *   causal        1: row i of a sequence sees rows 0..i; 0: all rows
+ *   scale         softmax scale, finite and > 0 (else KV_EINVAL)
  *   out           [total_tokens][num_q_heads][head_dim] bf16
  *   lse           [total_tokens][num_q_heads] fp32 or NULL
  * ------------------------------------------------------------------------- */
@@ -196,13 +204,30 @@ int prefill_attn(const void* q, const void* k, const void* v,
  *                 the chunk size beyond fp32 rounding.
  *   out           [total_new][num_q_heads][head_dim] bf16
  *   lse           [total_new][num_q_heads] fp32 or NULL
- *   workspace     >= extend_attn_workspace_bytes(...) bytes
+ *   scale         softmax scale, finite and > 0 (else KV_EINVAL)
+ *   workspace     >= extend_attn_workspace_bytes(...) bytes (0 in fused mode)
  * New token i of a request with C cached tokens sits at position C + i and
  * sees cached tokens 0..C-1 and new tokens 0..i.  Cache: NHD bf16.
+ * Table capacity (max_blocks_per_seq * block_size) at most 2^30 tokens.
+ *
+ * Two executions of the same algorithm (they differ only in fp32 rounding):
+ *  split  every (request, part) is its own work item: part 0 = the new tokens
+ *         among themselves, part c >= 1 = all new tokens against context
+ *         chunk c-1 (chunk = the request's share of the budget); each writes
+ *         an fp32 (o, lse) partial to the workspace and a final pass merges
+ *         them by log-sum-exp weights -- the pages' stages (1)-(3) literally,
+ *         with the chunks run in parallel.
+ *  fused  one workgroup walks the context chunks (the same key tiles in the
+ *         same order) and then the new tokens with one running softmax
+ *         state: the merge happens in registers and no workspace is used.
+ * extend_attn picks fused when the new tokens alone fill the GPU (or there is
+ * no context), else split; extend_attn_ex lets the caller choose.
  * ------------------------------------------------------------------------- */
 size_t extend_attn_workspace_bytes(const kv_cache_t* cache, int32_t num_seqs,
                                    int32_t total_new_tokens, int32_t num_q_heads,
                                    int32_t max_ctx_len, int32_t chunk_budget_tokens);
+
+typedef enum { KV_EXTEND_AUTO = 0, KV_EXTEND_SPLIT = 1, KV_EXTEND_FUSED = 2 } kv_extend_mode;
 int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new,
                 const void* v_new, const int32_t* cu_q_lens, const int32_t* ctx_lens,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -210,6 +235,20 @@ int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new,
                 int32_t max_ctx_len, int32_t num_q_heads, int32_t chunk_budget_tokens,
                 float scale, void* out, float* lse, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Same call with the execution chosen by the caller (mode: kv_extend_mode);
+ * the workspace query takes the same mode. */
+size_t extend_attn_workspace_bytes_ex(const kv_cache_t* cache, int32_t num_seqs,
+                                      int32_t total_new_tokens, int32_t num_q_heads,
+                                      int32_t max_ctx_len, int32_t chunk_budget_tokens,
+                                      int32_t mode);
+int extend_attn_ex(const kv_cache_t* cache, const void* q, const void* k_new,
+                   const void* v_new, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   int32_t num_seqs, int32_t total_new_tokens, int32_t max_q_len,
+                   int32_t max_ctx_len, int32_t num_q_heads, int32_t chunk_budget_tokens,
+                   float scale, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, int32_t mode, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Layer pack / unpack -- [PD] section "Architecture", write mode: after each

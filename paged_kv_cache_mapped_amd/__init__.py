@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 KV_OK, KV_EINVAL, KV_ENOSPC, KV_ENOTSUP, KV_EHIP = 0, -22, -28, -95, -1000
 KV_DTYPE_BF16, KV_DTYPE_FP8_E4M3 = 0, 1
 KV_LAYOUT_NHD, KV_LAYOUT_PRESHUFFLED = 0, 1
+KV_EXTEND_AUTO, KV_EXTEND_SPLIT, KV_EXTEND_FUSED = 0, 1, 2
+_EXTEND_MODES = {"auto": KV_EXTEND_AUTO, "split": KV_EXTEND_SPLIT, "fused": KV_EXTEND_FUSED}
 
 
 class PagedKVError(RuntimeError):
@@ -53,6 +55,9 @@ _SIGS = {
     "extend_attn_workspace_bytes": (_SZ, [_PC, _I32, _I32, _I32, _I32, _I32]),
     "extend_attn": (ctypes.c_int, [_PC, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                    _I32, _F, _P, _P, _P, _SZ, _P]),
+    "extend_attn_workspace_bytes_ex": (_SZ, [_PC, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "extend_attn_ex": (ctypes.c_int, [_PC, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                      _I32, _I32, _F, _P, _P, _P, _SZ, _I32, _P]),
     "kv_layer_packed_bytes": (_SZ, [_PC, _I32]),
     "kv_pack_layer": (ctypes.c_int, [_PC, _P, _I32, _P, _SZ, _P]),
     "kv_unpack_layer": (ctypes.c_int, [_PC, _P, _I32, _P, _SZ, _P]),
@@ -90,6 +95,34 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _want(t, name: str, dtypes, ndim: Optional[int] = None, optional: bool = False) -> None:
+    """Refuse a tensor the C ABI would misread: wrong element type, wrong rank
+    or not contiguous.  `dtypes` is a tuple of torch dtypes."""
+    if t is None:
+        if optional:
+            return
+        raise TypeError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, "
+                        f"got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors) -> None:
+    """Every given tensor (None skipped) lives in GPU memory."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _t():
+    import torch
+    return torch
+
+
 def _stream(t):
     import torch
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -107,6 +140,15 @@ class PagedKVCache:
     def __init__(self, k, v, block_size: int, num_kv_heads: int, head_dim: int,
                  layout: str = "nhd", dtype: str = "bf16", k_scale: float = 1.0,
                  v_scale: float = 1.0):
+        if layout not in ("nhd", "preshuffled") or dtype not in ("bf16", "fp8"):
+            raise ValueError(f"unknown layout/dtype {layout}/{dtype}")
+        t = _t()
+        want = (t.bfloat16,) if dtype == "bf16" else (t.uint8, t.float8_e4m3fn)
+        _want(k, "k_cache", want)
+        _want(v, "v_cache", want)
+        if k.numel() != v.numel() or k.shape[0] != v.shape[0]:
+            raise ValueError("k_cache and v_cache must hold the same blocks")
+        _on_gpu(k_cache=k, v_cache=v)
         self.k, self.v = k, v
         self.block_size, self.num_kv_heads, self.head_dim = block_size, num_kv_heads, head_dim
         self.layout, self.dtype = layout, dtype
@@ -124,6 +166,15 @@ class PagedKVCache:
 
 def kv_write(cache: PagedKVCache, k, v, slot_mapping) -> None:
     """Store k, v [T, H_kv, D] bf16 at slot_mapping [T] int64 (negative = skip)."""
+    t = _t()
+    _want(k, "k", (t.bfloat16,), 3)
+    _want(v, "v", (t.bfloat16,), 3)
+    _want(slot_mapping, "slot_mapping", (t.int64,), 1)
+    if k.shape != v.shape or slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("k, v and slot_mapping disagree on the number of tokens")
+    if k.shape[1] != cache.num_kv_heads or k.shape[2] != cache.head_dim:
+        raise ValueError("k/v heads or head_dim do not match the cache")
+    _on_gpu(k=k, v=v, slot_mapping=slot_mapping)
     d = cache.desc()
     _check(lib().kv_write(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(slot_mapping),
                           int(k.shape[0]), _stream(k)))
@@ -140,7 +191,17 @@ def paged_decode(cache: PagedKVCache, q, block_tables, seq_lens, max_seq_len: in
                  out=None, lse=None, workspace=None, split_tokens: int = 0):
     """q [B, H_q, D] bf16 -> (out [B, H_q, D] bf16, lse [B, H_q] fp32)."""
     import torch
+    _want(q, "q", (torch.bfloat16,), 3)
+    _want(block_tables, "block_tables", (torch.int32,), 2)
+    _want(seq_lens, "seq_lens", (torch.int32,), 1)
+    _want(out, "out", (torch.bfloat16,), 3, optional=True)
+    _want(lse, "lse", (torch.float32,), 2, optional=True)
+    _want(workspace, "workspace", (torch.uint8,), 1, optional=True)
     B, Hq, D = q.shape
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables / seq_lens must have one row per request")
+    _on_gpu(q=q, block_tables=block_tables, seq_lens=seq_lens, out=out, lse=lse,
+            workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -161,7 +222,15 @@ def prefill_attn(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: boo
                  out=None, lse=None):
     """Varlen prefill: q [T, H_q, D], k/v [T, H_kv, D] bf16, cu_seqlens [N+1] int32."""
     import torch
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _want(x, name, (torch.bfloat16,), 3)
+    _want(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    _want(out, "out", (torch.bfloat16,), 3, optional=True)
+    _want(lse, "lse", (torch.float32,), 2, optional=True)
     T, Hq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != T:
+        raise ValueError("q, k and v disagree on the number of tokens")
+    _on_gpu(q=q, k=k, v=v, cu_seqlens=cu_seqlens, out=out, lse=lse)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -173,34 +242,53 @@ def prefill_attn(q, k, v, cu_seqlens, max_seqlen: int, scale: float, causal: boo
 
 
 def extend_attn_workspace_bytes(cache: PagedKVCache, num_seqs: int, total_new: int,
-                                num_q_heads: int, max_ctx_len: int, chunk_budget_tokens: int) -> int:
+                                num_q_heads: int, max_ctx_len: int, chunk_budget_tokens: int,
+                                mode: str = "auto") -> int:
     d = cache.desc()
-    return int(lib().extend_attn_workspace_bytes(ctypes.byref(d), num_seqs, total_new, num_q_heads,
-                                                 max_ctx_len, chunk_budget_tokens))
+    return int(lib().extend_attn_workspace_bytes_ex(ctypes.byref(d), num_seqs, total_new,
+                                                    num_q_heads, max_ctx_len, chunk_budget_tokens,
+                                                    _EXTEND_MODES[mode]))
 
 
 def extend_attn(cache: PagedKVCache, q, k_new, v_new, cu_q_lens, ctx_lens, block_tables,
                 max_q_len: int, max_ctx_len: int, scale: float, chunk_budget_tokens: int = 32768,
-                out=None, lse=None, workspace=None):
+                out=None, lse=None, workspace=None, mode: str = "auto"):
     """Extend: q [T, H_q, D], k_new/v_new [T, H_kv, D] bf16; cached context
-    through block_tables.  Returns (out, lse)."""
+    through block_tables.  mode: "auto", "split" (per-chunk partials + LSE
+    merge pass) or "fused" (one running state per row block).
+    Returns (out, lse)."""
     import torch
+    for name, x in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _want(x, name, (torch.bfloat16,), 3)
+    _want(cu_q_lens, "cu_q_lens", (torch.int32,), 1)
+    _want(ctx_lens, "ctx_lens", (torch.int32,), 1)
+    _want(block_tables, "block_tables", (torch.int32,), 2, optional=True)
+    _want(out, "out", (torch.bfloat16,), 3, optional=True)
+    _want(lse, "lse", (torch.float32,), 2, optional=True)
+    _want(workspace, "workspace", (torch.uint8,), 1, optional=True)
+    if mode not in _EXTEND_MODES:
+        raise ValueError(f"mode must be one of {sorted(_EXTEND_MODES)}")
     T, Hq, D = q.shape
     E = int(cu_q_lens.shape[0]) - 1
+    if ctx_lens.shape[0] != E or (block_tables is not None and block_tables.shape[0] != E):
+        raise ValueError("ctx_lens / block_tables must have one row per request")
+    _on_gpu(q=q, k_new=k_new, v_new=v_new, cu_q_lens=cu_q_lens, ctx_lens=ctx_lens,
+            block_tables=block_tables, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    need = extend_attn_workspace_bytes(cache, E, T, Hq, max_ctx_len, chunk_budget_tokens)
+    need = extend_attn_workspace_bytes(cache, E, T, Hq, max_ctx_len, chunk_budget_tokens, mode)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     d = cache.desc()
     mb = int(block_tables.shape[1]) if block_tables is not None else 0
-    _check(lib().extend_attn(ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_q_lens),
-                             _ptr(ctx_lens), _ptr(block_tables), mb, E, T, int(max_q_len),
-                             int(max_ctx_len), Hq, int(chunk_budget_tokens), float(scale), _ptr(out),
-                             _ptr(lse), _ptr(workspace),
-                             int(workspace.numel() * workspace.element_size()), _stream(q)))
+    _check(lib().extend_attn_ex(ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                _ptr(cu_q_lens), _ptr(ctx_lens), _ptr(block_tables), mb, E, T,
+                                int(max_q_len), int(max_ctx_len), Hq, int(chunk_budget_tokens),
+                                float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                int(workspace.numel() * workspace.element_size()),
+                                _EXTEND_MODES[mode], _stream(q)))
     return out, lse
 
 
@@ -212,6 +300,9 @@ def kv_layer_packed_bytes(cache: PagedKVCache, n: int) -> int:
 def kv_pack_layer(cache: PagedKVCache, block_ids, dst=None):
     """Gather blocks block_ids [n] int32 of this layer into dst (uint8)."""
     import torch
+    _want(block_ids, "block_ids", (torch.int32,), 1)
+    _want(dst, "dst", (torch.uint8,), 1, optional=True)
+    _on_gpu(block_ids=block_ids, dst=dst)
     n = int(block_ids.shape[0])
     need = kv_layer_packed_bytes(cache, n)
     if dst is None:
@@ -224,6 +315,10 @@ def kv_pack_layer(cache: PagedKVCache, block_ids, dst=None):
 
 def kv_unpack_layer(cache: PagedKVCache, block_ids, src) -> None:
     """Scatter a packed buffer into blocks block_ids [n] int32 of this layer."""
+    t = _t()
+    _want(block_ids, "block_ids", (t.int32,), 1)
+    _want(src, "src", (t.uint8,), 1)
+    _on_gpu(block_ids=block_ids, src=src)
     d = cache.desc()
     _check(lib().kv_unpack_layer(ctypes.byref(d), _ptr(block_ids), int(block_ids.shape[0]),
                                  _ptr(src), int(src.numel() * src.element_size()), _stream(block_ids)))

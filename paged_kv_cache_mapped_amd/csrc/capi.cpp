@@ -65,6 +65,15 @@ int check_cache(const kv_cache_t* c, const char* fn) {
   return KV_OK;
 }
 
+// Softmax scale of the attention calls: a finite positive number.  (The
+// kernels take the running maximum of the raw scores and scale afterwards,
+// which is the maximum of the scaled scores only for a positive scale.)
+int check_scale(float scale, const char* fn) {
+  if (!(scale > 0.f) || !(scale <= 3.4e38f))
+    return fail(KV_EINVAL, "%s: scale must be finite and > 0 (got %g)", fn, (double)scale);
+  return KV_OK;
+}
+
 int check_heads(const kv_cache_t* c, int32_t num_q_heads, const char* fn) {
   if (num_q_heads <= 0) return fail(KV_EINVAL, "%s: num_q_heads must be > 0", fn);
   if (num_q_heads % c->num_kv_heads != 0)
@@ -115,7 +124,8 @@ size_t paged_decode_workspace_bytes_ex(const kv_cache_t* cache, int32_t batch,
                                        int32_t split_tokens) {
   if (decode_checks(cache, batch, num_q_heads, max_seq_len, split_tokens, "paged_decode_workspace_bytes"))
     return 0;
-  const pkv::DecodePlan p = pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens);
+  const pkv::DecodePlan p =
+      pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens, nullptr);
   return pkv::decode_workspace_bytes(p, batch, num_q_heads, cache->head_dim);
 }
 
@@ -141,8 +151,10 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32
                 (long long)max_blocks_per_seq * cache->block_size);
   if ((int64_t)max_blocks_per_seq * cache->block_size > (int64_t)1 << 30)
     return fail(KV_EINVAL, "%s: table capacity above 2^30 tokens", fn);
-  if (!(scale > 0.f) && !(scale < 0.f) && scale != 0.f) return fail(KV_EINVAL, "%s: scale is NaN", fn);
-  const pkv::DecodePlan p = pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens);
+  st = check_scale(scale, fn);
+  if (st) return st;
+  const pkv::DecodePlan p = pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens,
+                                             (hipStream_t)stream);
   const size_t need = pkv::decode_workspace_bytes(p, batch, num_q_heads, cache->head_dim);
   if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
   if (workspace_bytes < need)
@@ -173,6 +185,8 @@ int prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_
   if (head_dim != 128) return fail(KV_ENOTSUP, "%s: head_dim %d unsupported (128 only)", fn, head_dim);
   if (causal != 0 && causal != 1) return fail(KV_EINVAL, "%s: causal must be 0 or 1", fn);
   if (max_seqlen < 0) return fail(KV_EINVAL, "%s: max_seqlen < 0", fn);
+  int st = check_scale(scale, fn);
+  if (st) return st;
   if (num_seqs == 0 || max_seqlen == 0) return KV_OK;
   if (!q || !k || !v || !cu_seqlens || !out)
     return fail(KV_EINVAL, "%s: q, k, v, cu_seqlens and out must be non-NULL", fn);
@@ -185,7 +199,8 @@ int prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_
 }
 
 static int extend_checks(const kv_cache_t* cache, int32_t num_seqs, int32_t total_new,
-                         int32_t num_q_heads, int32_t max_ctx_len, int32_t budget, const char* fn) {
+                         int32_t num_q_heads, int32_t max_ctx_len, int32_t budget, int32_t mode,
+                         const char* fn) {
   int st = check_cache(cache, fn);
   if (st) return st;
   st = check_heads(cache, num_q_heads, fn);
@@ -195,28 +210,40 @@ static int extend_checks(const kv_cache_t* cache, int32_t num_seqs, int32_t tota
   if (num_seqs < 0 || total_new < 0 || max_ctx_len < 0)
     return fail(KV_EINVAL, "%s: negative size", fn);
   if (budget <= 0) return fail(KV_EINVAL, "%s: chunk_budget_tokens must be > 0", fn);
+  if (mode < KV_EXTEND_AUTO || mode > KV_EXTEND_FUSED)
+    return fail(KV_EINVAL, "%s: unknown mode %d", fn, mode);
   return KV_OK;
+}
+
+size_t extend_attn_workspace_bytes_ex(const kv_cache_t* cache, int32_t num_seqs, int32_t total_new,
+                                      int32_t num_q_heads, int32_t max_ctx_len, int32_t budget,
+                                      int32_t mode) {
+  if (extend_checks(cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget, mode,
+                    "extend_attn_workspace_bytes"))
+    return 0;
+  const pkv::ExtendPlan p =
+      pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget, mode, nullptr);
+  return pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
 }
 
 size_t extend_attn_workspace_bytes(const kv_cache_t* cache, int32_t num_seqs, int32_t total_new,
                                    int32_t num_q_heads, int32_t max_ctx_len, int32_t budget) {
-  if (extend_checks(cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget,
-                    "extend_attn_workspace_bytes"))
-    return 0;
-  const pkv::ExtendPlan p =
-      pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget);
-  return pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
+  return extend_attn_workspace_bytes_ex(cache, num_seqs, total_new, num_q_heads, max_ctx_len,
+                                        budget, KV_EXTEND_AUTO);
 }
 
-int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const void* v_new,
-                const int32_t* cu_q_lens, const int32_t* ctx_lens, const int32_t* block_tables,
-                int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_new, int32_t max_q_len,
-                int32_t max_ctx_len, int32_t num_q_heads, int32_t budget, float scale, void* out,
-                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+int extend_attn_ex(const kv_cache_t* cache, const void* q, const void* k_new, const void* v_new,
+                   const int32_t* cu_q_lens, const int32_t* ctx_lens, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_new,
+                   int32_t max_q_len, int32_t max_ctx_len, int32_t num_q_heads, int32_t budget,
+                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   int32_t mode, void* stream) {
   const char* fn = "extend_attn";
-  int st = extend_checks(cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget, fn);
+  int st = extend_checks(cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget, mode, fn);
   if (st) return st;
   if (max_q_len < 0) return fail(KV_EINVAL, "%s: max_q_len < 0", fn);
+  st = check_scale(scale, fn);
+  if (st) return st;
   if (num_seqs == 0 || total_new == 0 || max_q_len == 0) return KV_OK;
   if (!q || !k_new || !v_new || !cu_q_lens || !ctx_lens || !out)
     return fail(KV_EINVAL, "%s: q, k_new, v_new, cu_q_lens, ctx_lens and out must be non-NULL", fn);
@@ -224,11 +251,13 @@ int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const
     return fail(KV_EINVAL, "%s: block_tables needed when max_ctx_len > 0", fn);
   if (max_ctx_len > 0 && (int64_t)max_blocks_per_seq * cache->block_size < max_ctx_len)
     return fail(KV_EINVAL, "%s: max_ctx_len %d exceeds the table capacity", fn, max_ctx_len);
+  if ((int64_t)max_blocks_per_seq * cache->block_size > (int64_t)1 << 30)
+    return fail(KV_EINVAL, "%s: table capacity above 2^30 tokens", fn);
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return fail(KV_EINVAL, "%s: q, k_new, v_new and out must be 16-byte aligned", fn);
   if (num_q_heads > 65535 || num_seqs > 65535) return fail(KV_EINVAL, "%s: grid too large", fn);
-  const pkv::ExtendPlan p =
-      pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget);
+  const pkv::ExtendPlan p = pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len,
+                                             budget, mode, (hipStream_t)stream);
   const size_t need = pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
   if (need > 0) {
     if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
@@ -241,6 +270,17 @@ int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const
                                        max_q_len, num_q_heads, scale, out, lse, workspace,
                                        (hipStream_t)stream),
                     fn);
+}
+
+int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const void* v_new,
+                const int32_t* cu_q_lens, const int32_t* ctx_lens, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, int32_t num_seqs, int32_t total_new, int32_t max_q_len,
+                int32_t max_ctx_len, int32_t num_q_heads, int32_t budget, float scale, void* out,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return extend_attn_ex(cache, q, k_new, v_new, cu_q_lens, ctx_lens, block_tables,
+                        max_blocks_per_seq, num_seqs, total_new, max_q_len, max_ctx_len,
+                        num_q_heads, budget, scale, out, lse, workspace, workspace_bytes,
+                        KV_EXTEND_AUTO, stream);
 }
 
 size_t kv_layer_packed_bytes(const kv_cache_t* cache, int32_t n) {

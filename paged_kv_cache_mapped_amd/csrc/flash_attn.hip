@@ -135,8 +135,8 @@ __device__ __forceinline__ int64_t virtual_wg(const Args& a, int32_t r) {
   const int64_t m = (int64_t)r * J + ((r & 1) ? J - 1 - j : j);
   return m < (a.grid_pad >> 3) ? 8 * m + (blockIdx.x & 7) : -1;
 }
-static unsigned persistent_grid(int64_t grid_pad) {
-  const int64_t slots = 8 * (int64_t)(device_cu_count() / 8);
+static unsigned persistent_grid(int64_t grid_pad, hipStream_t stream) {
+  const int64_t slots = 8 * (int64_t)(device_cu_count(stream) / 8);
   return (unsigned)(grid_pad < slots ? grid_pad : slots);
 }
 
@@ -207,14 +207,26 @@ __device__ __forceinline__ int lane_here() {
 // 64 lanes' 16-byte global pieces into one contiguous 1 KB of LDS (lane i at
 // m0 + 16 i), with no staging registers.  Not known to the compiler: the
 // caller waits for them (vmcnt) before the barrier that publishes the stage.
-// m0 is a reserved register that the compiler sets right before each
-// instruction of its own that reads it, so overwriting it here is safe.
+// m0 is a reserved register the compiler may not list as clobbered, so each
+// copy saves it into a scratch SGPR and restores it afterwards: whatever the
+// compiler keeps in m0 survives the copy.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* g) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(g)
+      : "memory");
 }
 __device__ __forceinline__ void dma16s(uint32_t lds_base, uint32_t voff, const void* sbase) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
-               : "memory");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "memory");
 }
 __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -987,7 +999,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.grid_pad = work_grid(a.items, a.n_qitems);
   a.qt_major = causal ? 1 : 0;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid(persistent_grid(a.grid_pad));
+  const dim3 grid(persistent_grid(a.grid_pad, s));
   if (causal)
     hipLaunchKernelGGL(prefill_stream_kernel<true>, grid, dim3(kThreads), 0, s, a);
   else
@@ -996,7 +1008,8 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
 }
 
 ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
-                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens) {
+                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens,
+                       int32_t mode, hipStream_t stream) {
   ExtendPlan p;
   // Per-request share of the budget, rounded down to whole key tiles and
   // blocks (at least one).
@@ -1008,11 +1021,16 @@ ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
   p.chunk_tokens = (int32_t)share;
   p.n_chunks = max_ctx_len > 0 ? (int32_t)((max_ctx_len + share - 1) / share) : 0;
   p.n_parts = p.n_chunks + 1;
-  // Fused when the query tiles alone give every CU two rounds of its two
-  // resident workgroups; otherwise the context chunks become extra grid
-  // parallelism and a merge pass combines them.
+  // Automatic: fused when the query tiles alone give every CU two rounds of
+  // its two resident workgroups; otherwise the context chunks become extra
+  // grid parallelism and a merge pass combines them.
   const int64_t tiles = (int64_t)num_q_heads * ((total_new + kBM - 1) / kBM);
-  p.fused = (p.n_chunks == 0 || tiles >= (int64_t)4 * device_cu_count()) ? 1 : 0;
+  if (mode == KV_EXTEND_SPLIT)
+    p.fused = 0;
+  else if (mode == KV_EXTEND_FUSED)
+    p.fused = 1;
+  else
+    p.fused = (p.n_chunks == 0 || tiles >= (int64_t)4 * device_cu_count(stream)) ? 1 : 0;
   return p;
 }
 

@@ -9,12 +9,21 @@
 
 namespace pkv {
 
-// Compute units of the current device (256 on MI355X); host query, no sync.
-inline int32_t device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+// Compute units of the device that `stream` belongs to (the current device for
+// the null stream; 256 on MI355X).  Host queries only, no synchronisation; the
+// answer is cached per device.
+inline int32_t device_cu_count(hipStream_t stream) {
+  static int32_t cached[64] = {};
+  int dev = 0;
+  if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+  }
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] > 0) return cached[dev];
+  int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
+    n = 256;
+  cached[dev] = n;
   return n;
 }
 
@@ -29,17 +38,17 @@ hipError_t launch_pack(const kv_cache_t& c, const int32_t* ids, int32_t n, void*
 // ----------------------------------------------------------------- decode
 struct DecodePlan {
   int32_t split_tokens;      // fixed piece length requested by the caller (0 = automatic)
-  int32_t n_splits;          // = n_slots
   int32_t n_gchunks;         // ceil(G / 16) groups of query heads per KV head
   int32_t fixed_len;         // piece length if fixed, else 0
   int32_t len_min, len_max;  // bounds of the automatic piece length
   int32_t pieces_per_group;  // grid x: workgroups along the token stream
-  int32_t gpw;               // head groups per workgroup (1, 2 or 4)
-  int32_t n_slots;           // partial slots per (request, head)
+  int32_t gpw;               // head groups per workgroup (1, 2, 4 or 8)
+  int32_t target_pieces;     // pieces the automatic length aims at
   int32_t max_pieces;        // upper bound of the number of pieces
+  int32_t part_rows;         // partial (o, lse) rows per query head: max_pieces + batch
 };
 DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
-                       int32_t max_seq_len, int32_t split_tokens);
+                       int32_t max_seq_len, int32_t split_tokens, hipStream_t stream);
 size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_heads,
                               int32_t head_dim);
 hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
@@ -60,7 +69,8 @@ struct ExtendPlan {
   int32_t fused;          // 1: one workgroup runs every part of its rows (no partials)
 };
 ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
-                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens);
+                       int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens,
+                       int32_t mode, hipStream_t stream);
 size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
                               int32_t head_dim);
 hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,

@@ -28,7 +28,10 @@
 //     straight into registers.
 // At the end of a segment the wave writes either the final output (a request
 // inside one piece) or an fp32 partial (o, lse) that a second kernel merges
-// with LSE weights.  (Merging in the last piece to finish would need
+// with LSE weights.  The partial of piece p of request b goes to row p + b:
+// a request's pieces are consecutive and the next request starts at or after
+// the last piece of the previous one, so rows never collide and at most
+// (number of pieces + batch) rows exist, whatever the lengths.  (Merging in the last piece to finish would need
 // device-scope fences, which on this multi-XCD part write back and invalidate
 // whole L2 caches: far slower than a second launch.)
 //
@@ -59,13 +62,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   __bf16* out;
   float* lse;
-  float* part_o;              // [B][Hq][n_slots][D]
-  float* part_lse;            // [B][Hq][n_slots]
+  float* part_o;              // [part_rows][Hq][D]: row p + b for piece p of request b
+  float* part_lse;            // [part_rows][Hq]
   int32_t* hdr;               // [0] padded total T, [1] piece length, [2] pieces
   int32_t* cum;               // [B+1] exclusive prefix sums of lengths rounded up to 32
   int32_t* first_seq;         // [max_pieces] first request touched by each piece
   int32_t max_blocks, num_blocks, bs, bs_log2, Hkv, Hq, G, n_gchunks;
-  int32_t n_slots, batch, fixed_len, len_min, len_max, target_pieces;
+  int32_t batch, fixed_len, len_min, len_max, target_pieces;
   int32_t max_len;            // lengths are clamped to min(table capacity, max_seq_len)
   int32_t lds_plan;           // 1: every workgroup plans in LDS (batch <= kPlanLdsMax)
   int32_t gpw;                // head groups per workgroup (1, 2 or 4); 4 / gpw waves share a group
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 // For each request its piece overlaps, a wave stages the segment's block ids in its own LDS slice,
 // streams the segment's 32-token tiles through a two-deep register pipeline,
 // and writes either the final output (a request covered by one piece) or an
-// fp32 partial (o, lse) in slot (piece - first piece of the request).  No
+// fp32 partial (o, lse) in row p + b.  No
 // barrier is taken after the plan, so the waves of a CU drift apart and each
 // one's request boundaries are covered by the others' streaming.
 //
@@ -477,7 +480,6 @@ void decode_piece_kernel(DecodeArgs a) {
       if (t_begin >= t_end) continue;                    // only padding of b
       const int32_t first_piece = cb / len;
       const int32_t n_b = (cb + L - 1) / len - first_piece + 1;
-      const int32_t slot = p - first_piece;
 
       // segment prologue: this wave's block-id slice and Q, issued together.
       // The slice goes to the wave's own LDS rows; a wave's LDS accesses
@@ -550,10 +552,11 @@ void decode_piece_kernel(DecodeArgs a) {
           }
           if (q4 == 0 && a.lse) a.lse[bh] = lse_v;
         } else {
-          float* po = a.part_o + (bh * a.n_slots + slot) * kD;
+          const int64_t prow = (int64_t)(p + b) * a.Hq + h_base + r;
+          float* po = a.part_o + prow * kD;
 #pragma unroll
           for (int n = 0; n < 8; ++n) *(f32x4_t*)(po + 16 * n + 4 * q4) = st.o[n] * f;
-          if (q4 == 0) a.part_lse[bh * a.n_slots + slot] = lse_v;
+          if (q4 == 0) a.part_lse[prow] = lse_v;
         }
       }
     }
@@ -562,20 +565,30 @@ void decode_piece_kernel(DecodeArgs a) {
 
 // Second pass: o = sum_i w_i o_i / sum_i w_i with w_i = exp(lse_i - max lse),
 // lse = max + ln sum_i w_i, over the pieces of each request that spans more
-// than one piece.  One wave per (request, query head).
+// than one piece.  One wave per (request, query head).  A request of length 0
+// has no visible key: its output is 0 and its lse -inf.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
   if (bh >= (int64_t)a.batch * a.Hq) return;
   const int32_t b = (int32_t)(bh / a.Hq);
+  const int32_t h = (int32_t)(bh - (int64_t)b * a.Hq);
   const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
-  if (L == 0) return;
+  if (L == 0) {
+    *(bf16x2_t*)(a.out + bh * kD + 2 * lane) = bf16x2_t{(__bf16)0.f, (__bf16)0.f};
+    if (lane == 0 && a.lse) a.lse[bh] = kNegInf;
+    return;
+  }
   const int32_t len = a.hdr[1];
   const int32_t cb = a.cum[b];
   const int32_t n_b = (cb + L - 1) / len - cb / len + 1;
   if (n_b <= 1) return;                      // written by the main pass
-  const float* pl = a.part_lse + bh * a.n_slots;
-  const f32x2_t* po = (const f32x2_t*)(a.part_o + bh * a.n_slots * kD) + lane;
+  // partial rows (first piece + i + b), i < n_b; consecutive rows are Hq apart
+  const int64_t row0 = (int64_t)(cb / len + b) * a.Hq + h;
+  const float* pl = a.part_lse + row0;
+  const f32x2_t* po = (const f32x2_t*)(a.part_o + row0 * kD) + lane;
+  const int64_t ostride = (int64_t)a.Hq * (kD / 2);   // in f32x2 units
   float M = kNegInf;
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
@@ -585,8 +598,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     f32x2_t ov[kU];
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
-      lv[i] = i < n_b ? pl[i] : kNegInf;
-      ov[i] = i < n_b ? po[i * (kD / 2)] : f32x2_t{0.f, 0.f};
+      lv[i] = i < n_b ? pl[i * a.Hq] : kNegInf;
+      ov[i] = i < n_b ? po[i * ostride] : f32x2_t{0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < kU; ++i) M = fmaxf(M, lv[i]);
@@ -597,16 +610,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       acc += w * ov[i];
     }
   } else {
-    for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i]);
+    for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i * a.Hq]);
     for (int i = 0; i < n_b; ++i) {
-      const float w = fast_exp2((pl[i] - M) * kLog2e);
+      const float w = fast_exp2((pl[i * a.Hq] - M) * kLog2e);
       wsum += w;
-      acc += w * po[i * (kD / 2)];
+      acc += w * po[i * ostride];
     }
   }
   const float inv = 1.f / wsum;
   const __bf16 o0 = (__bf16)(acc[0] * inv), o1 = (__bf16)(acc[1] * inv);
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   *(bf16x2_t*)(a.out + bh * kD + 2 * lane) = bf16x2_t{o0, o1};
   if (lane == 0 && a.lse) a.lse[bh] = M + __log2f(wsum) * kLn2;
 }
@@ -620,7 +632,7 @@ static int32_t log2_ceil(int32_t v) {
 }
 
 DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
-                       int32_t max_seq_len, int32_t split_tokens) {
+                       int32_t max_seq_len, int32_t split_tokens, hipStream_t stream) {
   DecodePlan p;
   const int32_t G = num_q_heads / c.num_kv_heads;
   p.n_gchunks = (G + 15) / 16;
@@ -640,14 +652,25 @@ DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
   // workgroup's waves read the heads of the same tokens together
   p.gpw = groups % 8 == 0 ? 8 : (groups % 4 == 0 ? 4 : (groups % 2 == 0 ? 2 : 1));
   // grid: one round of one resident workgroup per CU
-  const int32_t slots = device_cu_count();
+  const int32_t slots = device_cu_count(stream);
   const int32_t rows = groups / p.gpw;
   p.pieces_per_group = slots / rows > 0 ? slots / rows : 1;   // grid x
   p.split_tokens = p.fixed_len;
-  p.n_slots = (max_seq_len + p.len_min - 1) / p.len_min + 1;
+  p.target_pieces = p.pieces_per_group * (kWaves / p.gpw);
+  // Pieces of the padded stream (T <= batch * max_seq_len rounded up to 32):
+  // a fixed length gives ceil(T / len); the automatic length is at least
+  // T / target_pieces unless clamped to len_max, so at most
+  // max(target_pieces, ceil(T / len_max)).
   const int64_t padded = (int64_t)batch * ((max_seq_len + 31) & ~31);
-  p.max_pieces = (int32_t)((padded + p.len_min - 1) / p.len_min) + 1;
-  p.n_splits = p.n_slots;
+  int64_t np;
+  if (p.fixed_len > 0) {
+    np = (padded + p.fixed_len - 1) / p.fixed_len;
+  } else {
+    np = (padded + p.len_max - 1) / p.len_max;
+    if (np < p.target_pieces) np = p.target_pieces;
+  }
+  p.max_pieces = (int32_t)(np + 1);
+  p.part_rows = p.max_pieces + batch;
   return p;
 }
 
@@ -655,7 +678,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_heads,
                               int32_t head_dim) {
-  const size_t rows = (size_t)batch * num_q_heads * p.n_slots;
+  const size_t rows = (size_t)p.part_rows * num_q_heads;
   return 256 + align256((size_t)(batch + 1) * 4) + align256((size_t)p.max_pieces * 4) +
          align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -680,7 +703,7 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   w += align256((size_t)(batch + 1) * 4);
   a.first_seq = (int32_t*)w;
   w += align256((size_t)p.max_pieces * 4);
-  const size_t rows = (size_t)batch * num_q_heads * p.n_slots;
+  const size_t rows = (size_t)p.part_rows * num_q_heads;
   a.part_o = (float*)w;
   w += align256(rows * c.head_dim * sizeof(float));
   a.part_lse = (float*)w;
@@ -694,13 +717,12 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   a.Hq = num_q_heads;
   a.G = num_q_heads / c.num_kv_heads;
   a.n_gchunks = p.n_gchunks;
-  a.n_slots = p.n_slots;
   a.batch = batch;
   a.fixed_len = p.fixed_len;
   a.len_min = p.len_min;
   a.len_max = p.len_max;
   a.gpw = p.gpw;
-  a.target_pieces = p.pieces_per_group * (kWaves / p.gpw);
+  a.target_pieces = p.target_pieces;
   a.qk_mult = scale * c.k_scale * kLog2e;
   a.v_scale = c.v_scale;
   a.lds_plan = batch <= kPlanLdsMax ? 1 : 0;

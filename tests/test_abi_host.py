@@ -112,20 +112,40 @@ def test_decode_argument_errors():
 
 
 def test_decode_workspace_closed_form():
-    """header + prefix sums + piece list + fp32 partial slots (o then lse)."""
+    """header + prefix sums + piece list + fp32 partial rows (o then lse).
+    Piece p of request b keeps its partial in row p + b, so there are at most
+    (pieces + batch) rows per query head whatever the lengths."""
     c = _cache(num_kv_heads=8)
     L = pk.lib()
     B, Hq, msl = 64, 64, 8192
     a256 = lambda x: -(-x // 256) * 256
+
+    def want(max_pieces):
+        rows = (max_pieces + B) * Hq
+        return 256 + a256(4 * (B + 1)) + a256(4 * max_pieces) + a256(rows * 128 * 4) + a256(rows * 4)
+
     for split in (128, 512, 1024):
-        n_slots = -(-msl // split) + 1
-        max_pieces = -(-(B * msl) // split) + 1
-        rows = B * Hq * n_slots
-        want = 256 + a256(4 * (B + 1)) + a256(4 * max_pieces) + a256(rows * 128 * 4) + a256(rows * 4)
-        assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, Hq, msl, split) == want
+        assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, Hq, msl, split) == \
+            want(-(-(B * msl) // split) + 1)
+    # automatic pieces (no GPU here: 256 compute units assumed): 8 KV heads of
+    # 8 query heads -> one workgroup row of 256 workgroups x 1 wave per group
+    # -> 256 target pieces; the longest piece a wave's table slice holds at
+    # block size 16 is 4064 tokens
+    assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, Hq, msl, 0) == \
+        want(max(256, -(-(B * msl) // 4064)) + 1)
     assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), B, 63, msl, 0) == 0   # invalid -> 0
     # batch * max_seq_len at 2^31 is rejected
     assert L.paged_decode_workspace_bytes_ex(ctypes.byref(c), 65535, Hq, 1 << 16, 0) == 0
+
+
+def test_decode_workspace_bounded_for_long_requests():
+    """The partial rows no longer scale with max_seq_len / 256 per request:
+    the fp8 preshuffled workload's shape (batch 128, 64:4, up to 16000
+    tokens) needs about 21 MB, not the 270 MB of one slot per 256 tokens."""
+    f = _cache(num_kv_heads=4, dtype=pk.KV_DTYPE_FP8_E4M3, layout=pk.KV_LAYOUT_PRESHUFFLED, x=16,
+               k_scale=0.1, v_scale=0.1, num_blocks=131072)
+    n = pk.lib().paged_decode_workspace_bytes_ex(ctypes.byref(f), 128, 64, 16000, 0)
+    assert 0 < n < 32 << 20
 
 
 def test_pack_sizes_and_errors():
@@ -152,12 +172,50 @@ def test_prefill_and_extend_argument_errors():
     assert L.prefill_attn(None, None, None, None, 0, 0, 8, 2, 128, 0.1, 1, None, None, None) == pk.KV_OK
     c = _cache()
     f = _cache(dtype=pk.KV_DTYPE_FP8_E4M3, k_scale=0.1, v_scale=0.1)
-    ext = lambda cc, budget=32768, mctx=100, mb=16: L.extend_attn(
-        ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mb, 2, 64, 32, mctx, 8, budget, 0.1,
-        FAKE, None, FAKE, 1 << 30, None)
-    assert ext(f) == pk.KV_ENOTSUP
+    ext = lambda cc, budget=32768, mctx=100, mb=16, mode=0, scale=0.1: L.extend_attn_ex(
+        ctypes.byref(cc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mb, 2, 64, 32, mctx, 8, budget, scale,
+        FAKE, None, FAKE, 1 << 30, mode, None)
     assert ext(c, budget=0) == pk.KV_EINVAL
     assert ext(c, mctx=1000, mb=16) == pk.KV_EINVAL   # table too narrow for the context
+    assert ext(c, mode=3) == pk.KV_EINVAL
+    assert ext(c, mode=-1) == pk.KV_EINVAL
+    # a table of more than 2^30 tokens would overflow the kernels' 32-bit
+    # token arithmetic
+    assert ext(c, mb=(1 << 26) + 1) == pk.KV_EINVAL
+    assert "2^30" in _err()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("nan"), float("inf"), -float("inf")])
+def test_attention_calls_reject_bad_scales(scale):
+    """A softmax scale must be finite and positive in all three attention calls
+    (the tiles take the running maximum on raw scores)."""
+    L = pk.lib()
+    c = _cache()
+    rc = L.prefill_attn(FAKE, FAKE, FAKE, FAKE, 2, 100, 8, 2, 128, scale, 1, FAKE, None, None)
+    assert rc == pk.KV_EINVAL and "scale" in _err()
+    rc = L.extend_attn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 2, 64, 32, 100, 8,
+                       32768, scale, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == pk.KV_EINVAL and "scale" in _err()
+    rc = L.paged_decode(ctypes.byref(c), FAKE, 4, 8, FAKE, 32, FAKE, 512, scale, FAKE, None, FAKE,
+                        1 << 30, None)
+    assert rc == pk.KV_EINVAL and "scale" in _err()
+
+
+def test_extend_workspace_by_mode():
+    """Fused extend needs no workspace; split extend needs one fp32 (o, lse)
+    partial per (part, row, query head): parts = context chunks + 1."""
+    L = pk.lib()
+    c = _cache(num_kv_heads=8, num_blocks=16384)
+    a256 = lambda x: -(-x // 256) * 256
+    E, T, Hq, mctx, budget = 2, 16384, 64, 100000, 32768
+    ws = lambda mode: L.extend_attn_workspace_bytes_ex(ctypes.byref(c), E, T, Hq, mctx, budget, mode)
+    assert ws(pk.KV_EXTEND_FUSED) == 0
+    chunk = budget // E                               # 16384, a whole number of 64-key tiles
+    parts = -(-mctx // chunk) + 1                     # 7 chunks + the new tokens
+    rows = parts * T * Hq
+    assert ws(pk.KV_EXTEND_SPLIT) == a256(rows * 128 * 4) + a256(rows * 4)
+    assert ws(pk.KV_EXTEND_AUTO) in (0, ws(pk.KV_EXTEND_SPLIT))
+    assert ws(7) == 0                                 # invalid mode
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -176,3 +234,29 @@ def test_reorder_rejects_negative_lengths():
     with pytest.raises(pk.PagedKVError) as e:
         pk.reorder_batch([1, -2], [0, 0])
     assert e.value.code == pk.KV_EINVAL
+
+
+def test_binding_refuses_tensors_the_abi_would_misread():
+    """int64 lengths would be read as int32 pairs and a non-contiguous view with
+    the wrong row stride; the binding refuses both before any library call."""
+    import torch
+    q = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    tables = torch.zeros((2, 4), dtype=torch.int32)
+    with pytest.raises(TypeError, match="seq_lens"):
+        pk.paged_decode(None, q, tables, torch.ones(2, dtype=torch.int64), 16, 0.1)
+    with pytest.raises(ValueError, match="contiguous"):
+        pk.paged_decode(None, q, torch.zeros((4, 2), dtype=torch.int32).t(),
+                        torch.ones(2, dtype=torch.int32), 16, 0.1)
+    with pytest.raises(TypeError, match="q"):
+        pk.prefill_attn(q.float(), q, q, torch.zeros(2, dtype=torch.int32), 1, 0.1)
+    with pytest.raises(TypeError, match="cu_q_lens"):
+        pk.extend_attn(None, q, q, q, torch.zeros(2, dtype=torch.int64),
+                       torch.zeros(1, dtype=torch.int32), tables[:1], 2, 0, 0.1)
+    with pytest.raises(TypeError, match="slot_mapping"):
+        pk.kv_write(None, q, q, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(TypeError, match="k_cache"):
+        pk.PagedKVCache(torch.zeros((4, 16, 8, 128), dtype=torch.float16),
+                        torch.zeros((4, 16, 8, 128), dtype=torch.float16), 16, 8, 128)
+    with pytest.raises(ValueError, match="GPU"):      # right types, but host memory
+        pk.PagedKVCache(torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16),
+                        torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16), 16, 8, 128)

@@ -158,9 +158,9 @@ def test_decode_needle():
     _check(st, oracle_cache(st.cache), out, lse, BF16_TOL)
 
 
-def test_decode_llama70b_full_size_sampled():
-    """Batch 64, 64:8 heads, lengths in [2048, 8192], 32768 blocks; every
-    output computed on the GPU, 6 requests checked against the oracle."""
+def test_decode_llama70b_full_size():
+    """Batch 64, 64:8 heads, lengths in [2048, 8192], 32768 blocks: every
+    request checked against the oracle."""
     st = w.llama70b_decode_layer()
     say("decode llama70b full size")
     dc = device_cache(st.cache)
@@ -168,14 +168,12 @@ def test_decode_llama70b_full_size_sampled():
     ocache = oc.write(oracle_cache(st.cache), st.k_new, st.v_new, st.slot_mapping)
     out, lse = _run(dc, st)
     assert not np.isnan(out).any()
-    rows = list(np.random.default_rng(0).choice(st.batch, 6, replace=False))
-    rows += [int(np.argmax(st.seq_lens)), int(np.argmin(st.seq_lens))]
-    _check(st, ocache, out, lse, BF16_TOL, rows)
+    _check(st, ocache, out, lse, BF16_TOL)
 
 
-def test_decode_fp8_preshuffled_full_size_sampled():
+def test_decode_fp8_preshuffled_full_size():
     """Batch 128, 64:4 heads, lengths in [1000, 16000], fp8 e4m3 preshuffled
-    (x = 16), 131072 blocks; 6 requests checked against the oracle."""
+    (x = 16), 131072 blocks: every request checked against the oracle."""
     st = w.fp8_preshuffled_decode()
     say("decode fp8 preshuffled full size")
     dc = device_cache(st.cache)
@@ -183,6 +181,30 @@ def test_decode_fp8_preshuffled_full_size_sampled():
     ocache = oc.write(oracle_cache(st.cache), st.k_new, st.v_new, st.slot_mapping)
     out, lse = _run(dc, st)
     assert not np.isnan(out).any()
-    rows = list(np.random.default_rng(1).choice(st.batch, 6, replace=False))
-    rows += [int(np.argmax(st.seq_lens))]
-    _check(st, ocache, out, lse, FP8_TOL, rows)
+    _check(st, ocache, out, lse, FP8_TOL)
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_decode_empty_requests(split):
+    """Requests of length 0 see no key: out = 0 and lse = -inf (the output
+    buffer starts as NaN, so an unwritten row shows).  Their neighbours, in
+    the same pieces, are unaffected."""
+    t = torch()
+    st = w.decode_workload(15, 9, 16, 2, 128, 16, 9 * 40 + 64, 100, 600)
+    lens = st.seq_lens.copy()
+    lens[[0, 4, 5, 8]] = 0
+    st.seq_lens = lens
+    say(f"decode with empty requests split={split} lens={lens.tolist()}")
+    dc = device_cache(st.cache)
+    out = t.full((st.batch, 16, 128), float("nan"), dtype=t.bfloat16, device="cuda")
+    lse = t.full((st.batch, 16), float("nan"), dtype=t.float32, device="cuda")
+    pk.paged_decode(dc, dev(st.q), dev(st.block_tables), dev(st.seq_lens), int(lens.max()), st.scale,
+                    out=out, lse=lse, split_tokens=split)
+    t.cuda.synchronize()
+    o, l = bf16_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    empty = lens == 0
+    assert (o[empty] == 0).all() and np.isneginf(l[empty]).all()
+    _check(st, oracle_cache(st.cache), o, l, BF16_TOL, rows=list(np.flatnonzero(~empty)))
+    ro, rl = oa.paged_decode(ob.to_f64(st.q[empty]), oracle_cache(st.cache),
+                             st.block_tables[empty], lens[empty], st.scale)
+    assert (ro == 0).all() and np.isneginf(rl).all()        # the oracle's reading agrees

@@ -65,6 +65,7 @@ def test_write_then_gather_returns_written_tokens(layout, dtype):
         assert np.array_equal(K[pos], bf16.to_f64(kb)) and np.array_equal(V[pos], bf16.to_f64(vb))
     else:
         # dequantised codes are within half an fp8 step of the written values
+        # (the exact bytes are pinned by test_fp8_write_bytes_exact)
         kx = bf16.to_f64(kb)
         rel = np.abs(K[pos] - kx) / np.maximum(np.abs(kx), 2.0 ** -6 * c.k_scale)
         assert rel.max() <= 2.0 ** -4 + 1e-12
@@ -105,3 +106,61 @@ def test_pack_unpack(layout, dtype):
     # round trip in place
     c3 = oc.unpack_layer(c, ids, buf)
     assert np.array_equal(c3.k, c.k) and np.array_equal(c3.v, c.v)
+
+
+@pytest.mark.parametrize("layout", ["nhd", "preshuffled"])
+def test_fp8_write_bytes_exact(layout):
+    """The quantising write, byte for byte, against a cache image built
+    independently: each code is torch's float8_e4m3fn cast of the fp32 product
+    fl32(x) * fl32(1/scale) (a library conversion the oracle does not call),
+    and each code is placed by the layout formulas element by element:
+    NHD k[blk, off, h, d]; preshuffled k[blk, h, d // 16, off, d % 16] and
+    v[blk, h, off // 16, d, off % 16].  K and V use different scales (a factor
+    of 37 apart), so swapping them, or misplacing an element, changes bytes."""
+    import torch
+    rng = np.random.default_rng(17)
+    H, D, bs, nb, x = 2, 32, 16, 6, 16
+    k_scale, v_scale = 0.37, 0.01
+    if layout == "nhd":
+        kshape = vshape = (nb, bs, H, D)
+    else:
+        kshape, vshape = (nb, H, D // x, bs, x), (nb, H, bs // x, D, x)
+    k0 = rng.integers(0, 256, size=kshape, dtype=np.uint8) & 0x77      # finite codes
+    v0 = rng.integers(0, 256, size=vshape, dtype=np.uint8) & 0x77
+    c = oc.Cache(k0, v0, layout, "fp8", bs, H, D, x if layout != "nhd" else 0, k_scale, v_scale)
+    T = 9
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    slots[4] = -1                                                     # padding token
+    # values spread over the whole code range, kept below 448 * scale
+    kb = w.f32_to_bf16_bits((rng.standard_normal((T, H, D)) * 40.0 * k_scale).astype(np.float32))
+    vb = w.f32_to_bf16_bits((rng.standard_normal((T, H, D)) * 40.0 * v_scale).astype(np.float32))
+
+    def codes(bits, scale):
+        f = (bits.astype(np.uint32) << 16).view(np.float32)
+        y = f * (np.float32(1.0) / np.float32(scale))                  # fp32 product
+        assert np.all(np.abs(y) < 448)
+        return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy()
+
+    kc, vc = codes(kb, k_scale), codes(vb, v_scale)
+    want_k, want_v = k0.copy(), v0.copy()
+    for i in range(T):
+        s_ = int(slots[i])
+        if s_ < 0:
+            continue
+        blk, off = s_ // bs, s_ % bs
+        for h in range(H):
+            for d in range(D):
+                if layout == "nhd":
+                    want_k[blk, off, h, d] = kc[i, h, d]
+                    want_v[blk, off, h, d] = vc[i, h, d]
+                else:
+                    want_k[blk, h, d // x, off, d % x] = kc[i, h, d]
+                    want_v[blk, h, off // x, d, off % x] = vc[i, h, d]
+    got = oc.write(c, kb, vb, slots)
+    assert got.k.tobytes() == want_k.tobytes()
+    assert got.v.tobytes() == want_v.tobytes()
+    # the planted mistakes this pin exists for change bytes
+    swapped = oc.write(oc.Cache(k0, v0, layout, "fp8", bs, H, D, c.x, v_scale, k_scale),
+                       kb, vb, slots)
+    assert swapped.k.tobytes() != want_k.tobytes()
