@@ -165,6 +165,26 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch,
                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * paged_decode_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): paged_decode with the automatic piece length and no workspace
+ * argument.  The plan and the split partials live in a static scratch array
+ * of the library, 64 MiB per device (held by every device the library runs
+ * on until the process ends), whose address is looked up once per device on
+ * the first call there.  Nothing is allocated by the call.  A batch that
+ * needs more than 64 MiB of scratch (paged_decode_workspace_bytes) returns
+ * KV_ENOSPC.  All calls on one device share that array: calls that may
+ * overlap on one device (different streams, or other host threads) race and
+ * must be serialised by the caller.  The scratch needs no initialisation
+ * (every call rewrites what it reads).  Arguments as for paged_decode.
+ * ------------------------------------------------------------------------- */
+int paged_decode_noalloc(const kv_cache_t* cache, const void* q, int32_t batch,
+                         int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         int32_t max_seq_len, float scale, void* out, float* lse,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * prefill_attn -- [ROCm] section "Processing details of the three paths",
  * prefill path: Q, K, V in the standard [num_tokens, num_heads, head_dim]
  * layout; section "ROCM_AITER_FA": new sequences go to a variable-length

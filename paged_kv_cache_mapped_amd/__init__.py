@@ -51,6 +51,8 @@ _SIGS = {
     "paged_decode": (ctypes.c_int, [_PC, _P, _I32, _I32, _P, _I32, _P, _I32, _F, _P, _P, _P, _SZ, _P]),
     "paged_decode_ex": (ctypes.c_int, [_PC, _P, _I32, _I32, _P, _I32, _P, _I32, _F, _P, _P, _P, _SZ,
                                        _I32, _P]),
+    "paged_decode_noalloc": (ctypes.c_int, [_PC, _P, _I32, _I32, _P, _I32, _P, _I32, _F, _P, _P,
+                                            _P]),
     "prefill_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P]),
     "extend_attn_workspace_bytes": (_SZ, [_PC, _I32, _I32, _I32, _I32, _I32]),
     "extend_attn": (ctypes.c_int, [_PC, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -215,6 +217,27 @@ def paged_decode(cache: PagedKVCache, q, block_tables, seq_lens, max_seq_len: in
                                  float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                  int(workspace.numel() * workspace.element_size()),
                                  int(split_tokens), _stream(q)))
+    return out, lse
+
+
+def paged_decode_noalloc(cache: PagedKVCache, q, block_tables, seq_lens, max_seq_len: int,
+                         scale: float, out, lse=None):
+    """paged_decode into a caller-given `out` with the library's static
+    scratch instead of a workspace (no allocation anywhere in the call)."""
+    import torch
+    _want(q, "q", (torch.bfloat16,), 3)
+    _want(block_tables, "block_tables", (torch.int32,), 2)
+    _want(seq_lens, "seq_lens", (torch.int32,), 1)
+    _want(out, "out", (torch.bfloat16,), 3)
+    _want(lse, "lse", (torch.float32,), 2, optional=True)
+    B, Hq, D = q.shape
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B or out.shape != q.shape:
+        raise ValueError("block_tables / seq_lens / out must match q's batch")
+    _on_gpu(q=q, block_tables=block_tables, seq_lens=seq_lens, out=out, lse=lse)
+    d = cache.desc()
+    _check(lib().paged_decode_noalloc(ctypes.byref(d), _ptr(q), B, Hq, _ptr(block_tables),
+                                      int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                                      float(scale), _ptr(out), _ptr(lse), _stream(q)))
     return out, lse
 
 

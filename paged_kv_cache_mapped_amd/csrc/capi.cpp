@@ -134,12 +134,12 @@ size_t paged_decode_workspace_bytes(const kv_cache_t* cache, int32_t batch, int3
   return paged_decode_workspace_bytes_ex(cache, batch, num_q_heads, max_seq_len, 0);
 }
 
-int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32_t num_q_heads,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out,
-                    float* lse, void* workspace, size_t workspace_bytes, int32_t split_tokens,
-                    void* stream) {
-  const char* fn = "paged_decode";
+// Every check of a decode call that does not involve the workspace.
+static int decode_call_checks(const kv_cache_t* cache, const void* q, int32_t batch,
+                              int32_t num_q_heads, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t max_seq_len, float scale, const void* out,
+                              int32_t split_tokens, const char* fn) {
   int st = decode_checks(cache, batch, num_q_heads, max_seq_len, split_tokens, fn);
   if (st) return st;
   if (!q || !block_tables || !seq_lens || !out)
@@ -151,7 +151,28 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32
                 (long long)max_blocks_per_seq * cache->block_size);
   if ((int64_t)max_blocks_per_seq * cache->block_size > (int64_t)1 << 30)
     return fail(KV_EINVAL, "%s: table capacity above 2^30 tokens", fn);
-  st = check_scale(scale, fn);
+  return check_scale(scale, fn);
+}
+
+static int decode_launch(const kv_cache_t* cache, const pkv::DecodePlan& p, const void* q,
+                         int32_t batch, int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, void* out, float* lse, void* workspace, void* stream,
+                         const char* fn) {
+  return hip_status(pkv::launch_decode(*cache, p, q, batch, num_q_heads, block_tables,
+                                       max_blocks_per_seq, seq_lens, max_seq_len, scale, out, lse,
+                                       workspace, (hipStream_t)stream),
+                    fn);
+}
+
+int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out,
+                    float* lse, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                    void* stream) {
+  const char* fn = "paged_decode";
+  int st = decode_call_checks(cache, q, batch, num_q_heads, block_tables, max_blocks_per_seq,
+                              seq_lens, max_seq_len, scale, out, split_tokens, fn);
   if (st) return st;
   const pkv::DecodePlan p = pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, split_tokens,
                                              (hipStream_t)stream);
@@ -160,10 +181,8 @@ int paged_decode_ex(const kv_cache_t* cache, const void* q, int32_t batch, int32
   if (workspace_bytes < need)
     return fail(KV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   if (!aligned16(workspace)) return fail(KV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-  return hip_status(pkv::launch_decode(*cache, p, q, batch, num_q_heads, block_tables,
-                                       max_blocks_per_seq, seq_lens, max_seq_len, scale, out, lse,
-                                       workspace, (hipStream_t)stream),
-                    fn);
+  return decode_launch(cache, p, q, batch, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
+                       max_seq_len, scale, out, lse, workspace, stream, fn);
 }
 
 int paged_decode(const kv_cache_t* cache, const void* q, int32_t batch, int32_t num_q_heads,
@@ -172,6 +191,29 @@ int paged_decode(const kv_cache_t* cache, const void* q, int32_t batch, int32_t 
                  size_t workspace_bytes, void* stream) {
   return paged_decode_ex(cache, q, batch, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
                          max_seq_len, scale, out, lse, workspace, workspace_bytes, 0, stream);
+}
+
+int paged_decode_noalloc(const kv_cache_t* cache, const void* q, int32_t batch,
+                         int32_t num_q_heads, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                         float scale, void* out, float* lse, void* stream) {
+  const char* fn = "paged_decode_noalloc";
+  int st = decode_call_checks(cache, q, batch, num_q_heads, block_tables, max_blocks_per_seq,
+                              seq_lens, max_seq_len, scale, out, 0, fn);
+  if (st) return st;
+  const pkv::DecodePlan p =
+      pkv::plan_decode(*cache, batch, num_q_heads, max_seq_len, 0, (hipStream_t)stream);
+  const size_t need = pkv::decode_workspace_bytes(p, batch, num_q_heads, cache->head_dim);
+  if (need > pkv::kDecodeScratchBytes)
+    return fail(KV_ENOSPC,
+                "%s: this batch needs %zu bytes of decode scratch, more than the library's "
+                "%zu; use paged_decode with a caller workspace",
+                fn, need, pkv::kDecodeScratchBytes);
+  hipError_t e;
+  void* ws = pkv::decode_scratch((hipStream_t)stream, &e);
+  if (!ws) return hip_status(e == hipSuccess ? hipErrorUnknown : e, fn);
+  return decode_launch(cache, p, q, batch, num_q_heads, block_tables, max_blocks_per_seq, seq_lens,
+                       max_seq_len, scale, out, lse, ws, stream, fn);
 }
 
 int prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,

@@ -51,6 +51,9 @@ DecodePlan plan_decode(const kv_cache_t& c, int32_t batch, int32_t num_q_heads,
                        int32_t max_seq_len, int32_t split_tokens, hipStream_t stream);
 size_t decode_workspace_bytes(const DecodePlan& p, int32_t batch, int32_t num_q_heads,
                               int32_t head_dim);
+// Size of the library's static decode scratch (paged_decode_noalloc).
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+void* decode_scratch(hipStream_t stream, hipError_t* err);
 hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q,
                          int32_t batch, int32_t num_q_heads, const int32_t* tables,
                          int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,

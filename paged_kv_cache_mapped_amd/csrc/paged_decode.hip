@@ -38,10 +38,20 @@
 // fp8 (OCP e4m3fn) caches are decoded to bf16 in registers (exact) and the
 // per-tensor scales are applied to the scores (k_scale) and to the output
 // (v_scale): <q, c*ks> = ks <q, c>, sum p (c*vs) = vs sum p c.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
 namespace pkv {
+
+// Scratch memory of paged_decode_noalloc: the decode workspace (plan and fp32
+// partials) for callers that cannot allocate.  Every device that runs the
+// library holds one copy until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol: its device address, per device, comes from
+// hipGetSymbolAddress and is the only handle used for it.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
 namespace {
 
 constexpr int kD = 128;
@@ -748,6 +758,44 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
   const int64_t bh = (int64_t)batch * num_q_heads;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((bh + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace pkv
+
+namespace pkv {
+
+// Device address of `scratch` on the device `stream` runs on, looked up once
+// per device with that device current.  Returns nullptr (and the HIP error in
+// *err) when the lookup fails.
+void* decode_scratch(hipStream_t stream, hipError_t* err) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int cur = 0;
+  *err = hipGetDevice(&cur);
+  if (*err != hipSuccess) return nullptr;
+  int dev = cur;
+  if (stream != nullptr) {
+    *err = hipStreamGetDevice(stream, &dev);
+    if (*err != hipSuccess) return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    if (dev != cur && (*err = hipSetDevice(dev)) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (*err == hipSuccess) *err = e2;
+    }
+    if (*err != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  *err = hipSuccess;
+  return addr[dev];
 }
 
 }  // namespace pkv
