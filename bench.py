@@ -22,9 +22,23 @@ over one batch of seeded synthetic input that is already resident in HBM:
       scales in the preshuffled layout (x = 16), context lengths uniform in
       [1000, 16000].  Step = kv_write (quantising) + paged_decode.
       value = algorithmic HBM bytes / step time (GB/s).
-  long_context_extend: 2 x (100000 cached + 8192 new) tokens, 64:8 heads.
-The default run measures the headline and then, as "secondary" entries, the
-mixed batch and the fp8 preshuffled decode.
+  long_context_extend: 2 x (100000 cached + 8192 new) tokens, 64:8 heads,
+      32768-token chunk budget.  Step = kv_write + extend_attn.
+      value = new tokens / step time (tokens/s).
+  tiny_decode: batch 4, 8:2 heads, context [100, 512].  Step = kv_write +
+      paged_decode (launch-bound; reported in us).
+  decode_layout_compare: the Llama-3.1-70B decode layer's requests decoded
+      from the NHD cache and from the same values in the bf16 preshuffled
+      layout (x = 8).  Step = both decodes.
+The default run measures the headline and then every other workload as a
+"secondary" entry, each with its roofline and its CPU-oracle baseline.
+
+Per call, after the timed region: the average device time from HIP events
+around the call alone ("ms"), and for decode calls also with the L2 and MALL
+flushed before each call by a 512 MB read outside the event pair ("ms_cold",
+HBM rather than cache).  device_ms_per_step is the sum of the calls' device
+times, beside the host wall clock ms_per_step (their difference is launch and
+host overhead between calls).
 
 Roofline: the dominant call's algorithmic bytes (or flops) per launch divided
 by its average duration, from HIP events recorded around it in every timed
@@ -93,6 +107,26 @@ def counter_traffic(kernel, workload):
         return float(fields["traffic_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+def cpu_info():
+    """Host CPU model, logical CPU count and the BLAS thread count the oracle
+    runs with (numpy's matmul is its only multi-threaded part)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count() or 1, "blas_threads": int(blas)}
 
 
 class HipEvents:
@@ -197,7 +231,7 @@ def build_llama70b_decode_layer(torch, pk, w, dev):
         "kv_tokens": int(st.seq_lens.sum()), "pack_blocks": n,
     }
 
-    def cpu_sample(budget_s=12.0):
+    def cpu_sample(budget_s):
         from oracle import attention as oa, bf16 as ob, cache as oc
         ocache = oc.Cache(st.cache.k, st.cache.v, "nhd", "bf16", 16, Hkv, D)
         qf = ob.to_f64(st.q)
@@ -275,7 +309,7 @@ def build_qwen3_mixed_batch(torch, pk, w, dev):
         "query_tokens": T, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
     }
 
-    def cpu_sample(budget_s=12.0):
+    def cpu_sample(budget_s):
         from oracle import attention as oa, bf16 as ob, cache as oc
         ocache = oc.write(oc.Cache(mb.cache.k, mb.cache.v, "nhd", "bf16", 16, Hkv, D),
                           mb.k_new, mb.v_new, mb.slot_mapping)
@@ -325,7 +359,7 @@ def build_long_context_extend(torch, pk, w, dev):
                           "head_dim 128, bf16 NHD, block 16, 32768-token chunk budget",
               "query_tokens": T}
 
-    def cpu_sample(budget_s=12.0):
+    def cpu_sample(budget_s):
         from oracle import attention as oa, bf16 as ob, cache as oc
         ocache = oc.Cache(mb.cache.k, mb.cache.v, "nhd", "bf16", 16, Hkv, D)
         qf, kf, vf = ob.to_f64(mb.q), ob.to_f64(mb.k_new), ob.to_f64(mb.v_new)
@@ -372,7 +406,7 @@ def build_fp8_preshuffled_decode(torch, pk, w, dev):
         "kv_tokens": int(st.seq_lens.sum()),
     }
 
-    def cpu_sample(budget_s=12.0):
+    def cpu_sample(budget_s):
         from oracle import attention as oa, bf16 as ob, cache as oc
         ocache = oc.Cache(st.cache.k, st.cache.v, "preshuffled", "fp8", 16, Hkv, D, 16,
                           st.cache.k_scale, st.cache.v_scale)
@@ -390,11 +424,118 @@ def build_fp8_preshuffled_decode(torch, pk, w, dev):
     return calls, "paged_decode", "hbm", config, cpu_sample, ("GB/s", None)
 
 
+def build_tiny_decode(torch, pk, w, dev):
+    st = w.tiny_decode()
+    sp = st.cache.spec
+    dc = pk.PagedKVCache(dev(st.cache.k), dev(st.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim)
+    q, kn, vn = dev(st.q), dev(st.k_new), dev(st.v_new)
+    slots, tables, lens = dev(st.slot_mapping), dev(st.block_tables), dev(st.seq_lens)
+    msl = int(st.seq_lens.max())
+    B, Hq, D, Hkv = st.batch, st.num_q_heads, sp.head_dim, sp.num_kv_heads
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(pk.paged_decode_workspace_bytes(dc, B, Hq, msl), 16), dtype=torch.uint8,
+                     device=q.device)
+    row = Hkv * D * 2
+    kv_bytes = float(st.seq_lens.astype(np.int64).sum()) * row * 2
+    blocks = float(((st.seq_lens + 15) // 16).sum())
+    decode_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4 + blocks * 4 + B * 4
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), B * (2 * row * 2 + 8)),
+        Call("paged_decode", lambda: pk.paged_decode(dc, q, tables, lens, msl, st.scale, out=out,
+                                                     lse=lse, workspace=ws), decode_bytes),
+    ]
+    config = {"workload": "tiny decode: batch 4, 8:2 heads, head_dim 128, bf16 NHD, block 16, "
+                          "256 blocks, ctx U[100,512]; one write + decode step (launch-bound)",
+              "batch": B, "kv_tokens": int(st.seq_lens.sum())}
+
+    def cpu_sample(budget_s):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.Cache(st.cache.k, st.cache.v, "nhd", "bf16", 16, Hkv, D)
+        qf = ob.to_f64(st.q)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < budget_s:
+            oc.write(ocache, st.k_new, st.v_new, st.slot_mapping)
+            oa.paged_decode(qf, ocache, st.block_tables, st.seq_lens, st.scale)
+            n += 1
+        dt = time.perf_counter() - t0
+        return n * kv_bytes / dt / 1e9, f"{n} oracle write + decode steps of the whole batch; {dt:.1f} s"
+
+    return calls, "paged_decode", "hbm", config, cpu_sample, ("GB/s", None)
+
+
+def build_decode_layout_compare(torch, pk, w, dev):
+    """The decode layer's requests from two caches holding the same values:
+    NHD, and the bf16 preshuffled layout (x = 8) made from it by a permute."""
+    st = w.llama70b_decode_layer()
+    sp = st.cache.spec
+    nb, bs, Hkv, D = sp.num_blocks, sp.block_size, sp.num_kv_heads, sp.head_dim
+    k_nhd, v_nhd = dev(st.cache.k), dev(st.cache.v)
+    X = 8
+    # k[b, h, d // X, t, d % X] = K[b, t, h, d];  v[b, h, t // X, d, t % X] = V[b, t, h, d]
+    k_pre = k_nhd.view(nb, bs, Hkv, D // X, X).permute(0, 2, 3, 1, 4).contiguous()
+    v_pre = v_nhd.view(nb, bs // X, X, Hkv, D).permute(0, 3, 1, 4, 2).contiguous()
+    nhd = pk.PagedKVCache(k_nhd, v_nhd, bs, Hkv, D)
+    pre = pk.PagedKVCache(k_pre, v_pre, bs, Hkv, D, "preshuffled", "bf16")
+    q, tables, lens = dev(st.q), dev(st.block_tables), dev(st.seq_lens)
+    msl = int(st.seq_lens.max())
+    B, Hq = st.batch, st.num_q_heads
+    out_n, out_p = torch.empty_like(q), torch.empty_like(q)
+    lse_n = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    lse_p = torch.empty_like(lse_n)
+    wsn = torch.empty(max(pk.paged_decode_workspace_bytes(nhd, B, Hq, msl), 16), dtype=torch.uint8,
+                      device=q.device)
+    wsp = torch.empty_like(wsn)
+    row = Hkv * D * 2
+    kv_bytes = float(st.seq_lens.astype(np.int64).sum()) * row * 2
+    blocks = float(((st.seq_lens + 15) // 16).sum())
+    decode_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4 + blocks * 4 + B * 4
+    calls = [
+        Call("paged_decode_nhd", lambda: pk.paged_decode(nhd, q, tables, lens, msl, st.scale,
+                                                         out=out_n, lse=lse_n, workspace=wsn),
+             decode_bytes),
+        Call("paged_decode_preshuffled", lambda: pk.paged_decode(pre, q, tables, lens, msl,
+                                                                 st.scale, out=out_p, lse=lse_p,
+                                                                 workspace=wsp),
+             decode_bytes),
+    ]
+    config = {"workload": "llama-3.1-70b decode layer (batch 64, 64:8, ctx U[2048,8192], block 16) "
+                          "decoded from the bf16 NHD cache and from the same values in the bf16 "
+                          "preshuffled layout (x 8)",
+              "batch": B, "kv_tokens": int(st.seq_lens.sum())}
+
+    def cpu_sample(budget_s):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.Cache(st.cache.k, st.cache.v, "nhd", "bf16", 16, Hkv, D)
+        qf = ob.to_f64(st.q)
+        t0, done, n = time.perf_counter(), 0.0, 0
+        while time.perf_counter() - t0 < budget_s:
+            b = n % B
+            oa.paged_decode(qf[b:b + 1], ocache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
+                            st.scale)
+            done += float(st.seq_lens[b]) * row * 2
+            n += 1
+        dt = time.perf_counter() - t0
+        return done / dt / 1e9, f"oracle decode of {n} requests of this batch (NHD); {dt:.1f} s"
+
+    return calls, "paged_decode_preshuffled", "hbm", config, cpu_sample, ("GB/s", None)
+
+
 WORKLOADS = {
-    "long_context_extend": build_long_context_extend,
     "llama70b_decode_layer": build_llama70b_decode_layer,
     "qwen3_mixed_batch": build_qwen3_mixed_batch,
     "fp8_preshuffled_decode": build_fp8_preshuffled_decode,
+    "long_context_extend": build_long_context_extend,
+    "tiny_decode": build_tiny_decode,
+    "decode_layout_compare": build_decode_layout_compare,
+}
+SECONDARY_METRIC = {
+    "qwen3_mixed_batch": "mixed-batch attention tokens/s",
+    "fp8_preshuffled_decode": "paged decode HBM GB/s (fp8 preshuffled cache)",
+    "long_context_extend": "long-context extend tokens/s (chunked context, LSE merge)",
+    "tiny_decode": "paged decode HBM GB/s (tiny, launch-bound)",
+    "decode_layout_compare": "paged decode HBM GB/s, bf16 preshuffled vs NHD layout",
 }
 
 
@@ -406,8 +547,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama70b_decode_layer", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work per workload for cpu_baseline")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the mixed-batch measurement that follows the headline workload")
+                    help="measure only the chosen workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build runs its whole hot path on a single "
@@ -420,6 +563,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pk.lib()
+    # 512 MB read before each "cold" call: it replaces the L2 and MALL contents
+    # with clean lines (a fill would leave dirty lines whose write-back then
+    # lands inside the timed call)
+    flush_buf = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+    flush_sink = torch.zeros(1, dtype=torch.float32, device="cuda")
 
     def dev(a):
         if a.dtype == np.uint16:
@@ -461,19 +609,21 @@ def main():
         ms = (t1 - t0) * 1e3 / max(args.steps, 1)
         dom_ms = sum(hev.ms(a, b) for a, b in ev) / max(len(ev), 1)
 
+        def timed(c, cold):
+            evs = [(hev.new(), hev.new()) for _ in range(args.steps)]
+            for a, b in evs:
+                if cold:
+                    torch.sum(flush_buf, dim=0, keepdim=True, out=flush_sink)   # outside the events
+                hev.record(a, stream)
+                c.fn()
+                hev.record(b, stream)
+            torch.cuda.synchronize()
+            return sum(hev.ms(a, b) for a, b in evs) / max(len(evs), 1)
+
         # every call's own duration, from events around it, after the timed region
         per = {}
         for c in calls:
-            if c.name == dominant:
-                avg = dom_ms
-            else:
-                evs = [(hev.new(), hev.new()) for _ in range(args.steps)]
-                for a, b in evs:
-                    hev.record(a, stream)
-                    c.fn()
-                    hev.record(b, stream)
-                torch.cuda.synchronize()
-                avg = sum(hev.ms(a, b) for a, b in evs) / max(len(evs), 1)
+            avg = dom_ms if c.name == dominant else timed(c, False)
             d = {"ms": round(avg, 5)}
             if c.bytes:
                 d["GB/s"] = round(c.bytes / (avg * 1e-3) / 1e9, 1)
@@ -481,7 +631,13 @@ def main():
             if c.flops:
                 d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
                 d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+            if c.name.startswith("paged_decode"):
+                cold = timed(c, True)
+                d["ms_cold"] = round(cold, 5)
+                d["GB/s_cold"] = round(c.bytes / (cold * 1e-3) / 1e9, 1)
+                d["hbm_frac_cold"] = round(d["GB/s_cold"] / HBM_PEAK_GBS, 4)
             per[c.name] = d
+        device_ms = sum(per[c.name]["ms"] for c in calls)
 
         dom = next(c for c in calls if c.name == dominant)
         dms = dom_ms
@@ -489,7 +645,8 @@ def main():
             ach = dom.bytes / (dms * 1e-3) / 1e9
             roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": counter_traffic(dominant, name)}
+                    "traffic": counter_traffic(dominant.split("_nhd")[0].split("_preshuffled")[0],
+                                               name)}
         else:
             ach = dom.flops / (dms * 1e-3) / 1e12
             roof = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 1),
@@ -502,42 +659,42 @@ def main():
             value = tokens / (ms * 1e-3)
         cpu = None
         if with_cpu:
-            _log("timing the CPU oracle on a sample")
-            try:
-                from threadpoolctl import threadpool_info
-                cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-            except Exception:
-                cores = os.cpu_count() or 1
-            v, sample = cpu_sample()
-            cpu = {"value": round(v, 4), "unit": unit, "cores": int(cores), "kind": "oracle",
-                   "sample": sample}
+            _log(f"timing the CPU oracle on a sample of {name}")
+            info = cpu_info()
+            v, sample = cpu_sample(args.cpu_budget)
+            cpu = {"value": round(v, 4), "unit": unit, "cores": info["blas_threads"],
+                   "kind": "oracle", "sample": sample, "precision": "float64",
+                   "cpu_model": info["cpu_model"], "os_cpu_count": info["os_cpu_count"]}
         hev.close()
         # free this workload's device memory before the next one
         del calls
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        return {"value": value, "unit": unit, "ms": ms, "config": config, "roofline": roof,
-                "calls": per, "cpu": cpu}
+        return {"value": value, "unit": unit, "ms": ms, "device_ms": device_ms, "config": config,
+                "roofline": roof, "calls": per, "cpu": cpu}
 
-    main_r = measure(args.workload, not args.no_cpu_baseline)
+    with_cpu = not args.no_cpu_baseline
+    main_r = measure(args.workload, with_cpu)
     secondary = {}
     if args.workload == "llama70b_decode_layer" and not args.no_secondary:
-        r = measure("qwen3_mixed_batch", False)
-        secondary["qwen3_mixed_batch"] = {
-            "metric": "mixed-batch attention tokens/s", "value": round(r["value"], 1),
-            "unit": r["unit"], "ms_per_step": round(r["ms"], 4), "config": r["config"],
-            "roofline": r["roofline"], "calls": r["calls"]}
-        r = measure("fp8_preshuffled_decode", False)
-        secondary["fp8_preshuffled_decode"] = {
-            "metric": "paged decode HBM GB/s (fp8 preshuffled cache)", "value": round(r["value"], 1),
-            "unit": r["unit"], "ms_per_step": round(r["ms"], 4), "config": r["config"],
-            "roofline": r["roofline"], "calls": r["calls"]}
+        for name in SECONDARY_METRIC:
+            r = measure(name, with_cpu)
+            e = {"metric": SECONDARY_METRIC[name], "value": round(r["value"], 1),
+                 "unit": r["unit"], "ms_per_step": round(r["ms"], 4),
+                 "device_ms_per_step": round(r["device_ms"], 4), "config": r["config"],
+                 "roofline": r["roofline"], "cpu_baseline": r["cpu"], "calls": r["calls"]}
+            if name == "decode_layout_compare":
+                c = r["calls"]
+                e["preshuffled_vs_nhd"] = round(c["paged_decode_preshuffled"]["GB/s"] /
+                                                c["paged_decode_nhd"]["GB/s"], 4)
+            secondary[name] = e
     value, unit, ms, config = main_r["value"], main_r["unit"], main_r["ms"], main_r["config"]
     roof, per, cpu = main_r["roofline"], main_r["calls"], main_r["cpu"]
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "device_ms_per_step": round(main_r["device_ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded numpy PCG64; no datasets or weights)",
         "config": config, "roofline": roof, "cpu_baseline": cpu, "calls": per,
