@@ -30,6 +30,11 @@ over one batch of seeded synthetic input that is already resident in HBM:
   decode_layout_compare: the Llama-3.1-70B decode layer's requests decoded
       from the NHD cache and from the same values in the bf16 preshuffled
       layout (x = 8).  Step = both decodes.
+  heavy_tailed_mixed_batch: 64:4 heads, lognormal lengths (64 decodes, 12
+      extends with many short and a few long new-token runs, 2 prefills).
+      Step = kv_write + paged_decode + extend_attn + prefill_attn (three-way
+      routing); the same batch as ONE extend_attn call over every request is
+      timed beside it.
 The default run measures the headline and then every other workload as a
 "secondary" entry, each with its roofline and its CPU-oracle baseline.
 
@@ -522,6 +527,112 @@ def build_decode_layout_compare(torch, pk, w, dev):
     return calls, "paged_decode_preshuffled", "hbm", config, cpu_sample, ("GB/s", None)
 
 
+def unified_batch_args(mb):
+    """The whole reordered batch as ONE extend call (the single-kernel
+    alternative to three-way routing): a decode is an extend of 1 new token on
+    L - 1 cached tokens, a prefill an extend with no cached context."""
+    nd = mb.n_decode
+    qlens = np.concatenate([np.ones(nd, np.int64), np.diff(mb.ext_cu_q), np.diff(mb.pre_cu)])
+    ctx = np.concatenate([mb.dec_seq_lens - 1, mb.ext_ctx,
+                          np.zeros(len(mb.pre_cu) - 1, np.int64)]).astype(np.int32)
+    width = max(mb.dec_tables.shape[1] if nd else 1, mb.ext_tables.shape[1])
+    tables = np.full((len(qlens), width), mb.cache.poison_block, np.int32)
+    if nd:
+        tables[:nd, :mb.dec_tables.shape[1]] = mb.dec_tables
+    ne = len(mb.ext_ctx)
+    tables[nd:nd + ne, :mb.ext_tables.shape[1]] = mb.ext_tables
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    return cu, ctx, tables, int(qlens.max()), int(ctx.max())
+
+
+def build_heavy_tailed_mixed_batch(torch, pk, w, dev):
+    mb = w.heavy_tailed_mixed_batch()
+    sp = mb.cache.spec
+    dc = pk.PagedKVCache(dev(mb.cache.k), dev(mb.cache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim)
+    q, kn, vn, slots = dev(mb.q), dev(mb.k_new), dev(mb.v_new), dev(mb.slot_mapping)
+    d0, d1 = mb.rows_decode
+    e0, e1 = mb.rows_extend
+    p0, p1 = mb.rows_prefill
+    Hq, Hkv, D = mb.num_q_heads, sp.num_kv_heads, sp.head_dim
+    T = int(q.shape[0])
+    out = torch.empty_like(q)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    dtab, dlen = dev(mb.dec_tables), dev(mb.dec_seq_lens)
+    dmsl = int(mb.dec_seq_lens.max())
+    dws = torch.empty(max(pk.paged_decode_workspace_bytes(dc, d1 - d0, Hq, dmsl), 16),
+                      dtype=torch.uint8, device=q.device)
+    ecu, ectx, etab = dev(mb.ext_cu_q), dev(mb.ext_ctx), dev(mb.ext_tables)
+    E = int(mb.ext_ctx.size)
+    emq, emc = int(np.diff(mb.ext_cu_q).max()), int(mb.ext_ctx.max())
+    ews = torch.empty(max(pk.extend_attn_workspace_bytes(dc, E, e1 - e0, Hq, emc, 32768), 16),
+                      dtype=torch.uint8, device=q.device)
+    pcu = dev(mb.pre_cu)
+    pmax = int(np.diff(mb.pre_cu).max())
+    ucu, uctx, utab, umq, umc = unified_batch_args(mb)
+    ucu_d, uctx_d, utab_d = dev(ucu), dev(uctx), dev(utab)
+    uout = torch.empty_like(q)
+    ulse = torch.empty_like(lse)
+    uws = torch.empty(max(pk.extend_attn_workspace_bytes(dc, len(uctx), T, Hq, umc, 32768), 16),
+                      dtype=torch.uint8, device=q.device)
+
+    row = Hkv * D * 2
+    dec_bytes = float(mb.dec_seq_lens.astype(np.int64).sum()) * row * 2
+    ext_pairs = sum(int(n) * int(c) + int(n) * (int(n) + 1) // 2
+                    for n, c in zip(np.diff(mb.ext_cu_q), mb.ext_ctx))
+    pre_pairs = sum(int(n) * (int(n) + 1) // 2 for n in np.diff(mb.pre_cu))
+    dec_pairs = int(mb.dec_seq_lens.astype(np.int64).sum())
+    calls = [
+        Call("kv_write", lambda: pk.kv_write(dc, kn, vn, slots), T * (4 * row + 8)),
+        Call("paged_decode", lambda: pk.paged_decode(dc, q[d0:d1], dtab, dlen, dmsl, mb.scale,
+                                                     out=out[d0:d1], lse=lse[d0:d1], workspace=dws),
+             dec_bytes),
+        Call("extend_attn", lambda: pk.extend_attn(dc, q[e0:e1], kn[e0:e1], vn[e0:e1], ecu, ectx,
+                                                   etab, emq, emc, mb.scale, 32768, out=out[e0:e1],
+                                                   lse=lse[e0:e1], workspace=ews),
+             0.0, float(ext_pairs) * Hq * 4 * D),
+        Call("prefill_attn", lambda: pk.prefill_attn(q[p0:p1], kn[p0:p1], vn[p0:p1], pcu, pmax,
+                                                     mb.scale, True, out=out[p0:p1], lse=lse[p0:p1]),
+             0.0, float(pre_pairs) * Hq * 4 * D),
+    ]
+    # the same batch through one extend call over every request (not part of
+    # the step; timed per call for the comparison)
+    unified = Call("unified_extend_attn", lambda: pk.extend_attn(
+        dc, q, kn, vn, ucu_d, uctx_d, utab_d, umq, umc, mb.scale, 32768, out=uout, lse=ulse,
+        workspace=uws), 0.0, float(ext_pairs + pre_pairs + dec_pairs) * Hq * 4 * D)
+    config = {
+        "workload": "heavy-tailed mixed batch [decode:extend:prefill]: 64:4 heads, head_dim 128, "
+                    "bf16 NHD, block 16; lognormal lengths: 64 decodes (ctx median 2000), "
+                    "12 extends (new median 96, ctx median 3000), 2 prefills (median 1500)",
+        "query_tokens": T, "decode_ctx": mb.dec_seq_lens.tolist(),
+        "extend_new": np.diff(mb.ext_cu_q).tolist(), "extend_ctx": mb.ext_ctx.tolist(),
+        "prefill_len": np.diff(mb.pre_cu).tolist(),
+    }
+
+    def cpu_sample(budget_s):
+        from oracle import attention as oa, bf16 as ob, cache as oc
+        ocache = oc.write(oc.Cache(mb.cache.k, mb.cache.v, "nhd", "bf16", 16, Hkv, D),
+                          mb.k_new, mb.v_new, mb.slot_mapping)
+        qf, kf, vf = ob.to_f64(mb.q), ob.to_f64(mb.k_new), ob.to_f64(mb.v_new)
+        t0, n = time.perf_counter(), 0
+        rng = np.random.default_rng(0)
+        while time.perf_counter() - t0 < budget_s:     # random rows of the batch
+            r = int(rng.integers(0, T))
+            if r < d1:
+                oa.paged_decode(qf[r:r + 1], ocache, mb.dec_tables[r:r + 1],
+                                mb.dec_seq_lens[r:r + 1], mb.scale)
+            elif r < e1:
+                oa.extend(qf[e0:e1], kf[e0:e1], vf[e0:e1], mb.ext_cu_q, mb.ext_ctx, ocache,
+                          mb.ext_tables, mb.scale, rows=[r - e0])
+            else:
+                oa.prefill(qf[p0:p1], kf[p0:p1], vf[p0:p1], mb.pre_cu, mb.scale, rows=[r - p0])
+            n += 1
+        dt = time.perf_counter() - t0
+        return n / dt, f"oracle rows of {n} random query tokens of this batch (all 64 heads); {dt:.1f} s"
+
+    return calls, "extend_attn", "mfma", config, cpu_sample, ("tokens/s", T), [unified]
+
+
 WORKLOADS = {
     "llama70b_decode_layer": build_llama70b_decode_layer,
     "qwen3_mixed_batch": build_qwen3_mixed_batch,
@@ -529,6 +640,7 @@ WORKLOADS = {
     "long_context_extend": build_long_context_extend,
     "tiny_decode": build_tiny_decode,
     "decode_layout_compare": build_decode_layout_compare,
+    "heavy_tailed_mixed_batch": build_heavy_tailed_mixed_batch,
 }
 SECONDARY_METRIC = {
     "qwen3_mixed_batch": "mixed-batch attention tokens/s",
@@ -536,6 +648,8 @@ SECONDARY_METRIC = {
     "long_context_extend": "long-context extend tokens/s (chunked context, LSE merge)",
     "tiny_decode": "paged decode HBM GB/s (tiny, launch-bound)",
     "decode_layout_compare": "paged decode HBM GB/s, bf16 preshuffled vs NHD layout",
+    "heavy_tailed_mixed_batch": "mixed-batch attention tokens/s, heavy-tailed lengths, "
+                                "three-way routed vs one unified extend call",
 }
 
 
@@ -576,8 +690,9 @@ def main():
 
     def measure(name, with_cpu):
         _log(f"building workload {name}")
-        calls, dominant, bound, config, cpu_sample, (unit, tokens) = WORKLOADS[name](
-            torch, pk, w, dev)
+        built = WORKLOADS[name](torch, pk, w, dev)
+        calls, dominant, bound, config, cpu_sample, (unit, tokens) = built[:6]
+        extra = built[6] if len(built) > 6 else []     # timed per call only, not in the step
         torch.cuda.synchronize()
 
         def step():
@@ -638,6 +753,15 @@ def main():
                 d["hbm_frac_cold"] = round(d["GB/s_cold"] / HBM_PEAK_GBS, 4)
             per[c.name] = d
         device_ms = sum(per[c.name]["ms"] for c in calls)
+        for c in extra:
+            c.fn()
+            torch.cuda.synchronize()
+            avg = timed(c, False)
+            d = {"ms": round(avg, 5), "not_in_step": True}
+            if c.flops:
+                d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
+                d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
+            per[c.name] = d
 
         dom = next(c for c in calls if c.name == dominant)
         dms = dom_ms
@@ -667,7 +791,7 @@ def main():
                    "cpu_model": info["cpu_model"], "os_cpu_count": info["os_cpu_count"]}
         hev.close()
         # free this workload's device memory before the next one
-        del calls
+        del calls, extra, built
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         return {"value": value, "unit": unit, "ms": ms, "device_ms": device_ms, "config": config,
@@ -683,6 +807,12 @@ def main():
                  "unit": r["unit"], "ms_per_step": round(r["ms"], 4),
                  "device_ms_per_step": round(r["device_ms"], 4), "config": r["config"],
                  "roofline": r["roofline"], "cpu_baseline": r["cpu"], "calls": r["calls"]}
+            if name == "heavy_tailed_mixed_batch":
+                c = r["calls"]
+                routed = sum(c[k]["ms"] for k in ("paged_decode", "extend_attn", "prefill_attn"))
+                e["three_way_attention_ms"] = round(routed, 5)
+                e["unified_attention_ms"] = c["unified_extend_attn"]["ms"]
+                e["unified_vs_three_way_time"] = round(c["unified_extend_attn"]["ms"] / routed, 3)
             if name == "decode_layout_compare":
                 c = r["calls"]
                 e["preshuffled_vs_nhd"] = round(c["paged_decode_preshuffled"]["GB/s"] /

@@ -227,7 +227,10 @@ int prefill_attn(const void* q, const void* k, const void* v,
  *   scale         softmax scale, finite and > 0 (else KV_EINVAL)
  *   workspace     >= extend_attn_workspace_bytes(...) bytes (0 in fused mode)
  * New token i of a request with C cached tokens sits at position C + i and
- * sees cached tokens 0..C-1 and new tokens 0..i.  Cache: NHD bf16.
+ * sees cached tokens 0..C-1 and new tokens 0..i.  Caches: NHD (any block
+ * size) or preshuffled (block size 16), bf16 or fp8; the context is read in
+ * place through the block table (fp8 codes decoded and scaled on the way, no
+ * gather copy); the new tokens come from k_new / v_new (bf16).
  * Table capacity (max_blocks_per_seq * block_size) at most 2^30 tokens.
  *
  * Two executions of the same algorithm (they differ only in fp32 rounding):

@@ -247,8 +247,8 @@ static int extend_checks(const kv_cache_t* cache, int32_t num_seqs, int32_t tota
   if (st) return st;
   st = check_heads(cache, num_q_heads, fn);
   if (st) return st;
-  if (cache->layout != KV_LAYOUT_NHD || cache->dtype != KV_DTYPE_BF16)
-    return fail(KV_ENOTSUP, "%s: the extend path reads NHD bf16 caches", fn);
+  if (cache->layout == KV_LAYOUT_PRESHUFFLED && cache->block_size != 16)
+    return fail(KV_ENOTSUP, "%s: the extend path reads preshuffled caches of block size 16", fn);
   if (num_seqs < 0 || total_new < 0 || max_ctx_len < 0)
     return fail(KV_EINVAL, "%s: negative size", fn);
   if (budget <= 0) return fail(KV_EINVAL, "%s: chunk_budget_tokens must be > 0", fn);

@@ -86,6 +86,10 @@ struct AttnArgs {
   int64_t grid_pad;         // launched workgroups (multiple of 8)
   int32_t qt_major;         // work order inside an XCD's block of lanes
   float qk_mult;            // scale * log2(e)
+  // context scores and values of an fp8 cache: code * k_scale, code * v_scale
+  float ctx_qk_mult;        // scale * k_scale * log2(e)
+  float ctx_vexp;           // log2(v_scale): added to the exponent of p
+  float ctx_linv;           // 1 / v_scale: takes it back out of the row sum
 };
 
 // Work order.  A work item is (lane, query item), lanes being the
@@ -260,6 +264,131 @@ __device__ __forceinline__ void dma_wait_for(int32_t& lookup) {
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(lookup)::"memory");
 }
 
+// Cache kinds of the extend's cached context.  NHD bf16 rows already are the
+// LDS rows the core reads, so the copy engine moves them as they are.  The
+// other kinds are loaded into registers one tile ahead (issued at the start
+// of a tile, stored at its end), decoded to bf16 -- exact: every e4m3fn value
+// is a bf16 value -- and written into the same LDS rows, so the core is the
+// same for every cache ("Beyond just running: native inference optimisation
+// in vLLM on AMD ROCm", section "ROCM_AITER_FA": the preshuffled layout
+// k [block][head][D/x][block_size][x], v [block][head][block_size/x][D][x];
+// the pages gather it into a contiguous copy first, this reads it in place).
+enum : int { kCtxNhdBf16 = 0, kCtxNhdFp8 = 1, kCtxPreBf16 = 2, kCtxPreFp8 = 3 };
+
+// One thread's share of a context tile in flight (raw cache bytes).
+struct Staged {
+  u32x4_t k[2], v[2];
+};
+
+// Issue the loads of this thread's share of the 64-key context tile at k0.
+//  NHD fp8: thread t takes 16 dims (16 bytes) of K and V of key t / 8; keys
+//    past kend repeat the last key, as in the copy-engine path.
+//  preshuffled (block size 16): thread t works in the tile's block t / 128
+//    (a block wholly past kend is read from block 0 and zeroed when stored,
+//    so no table entry past the range is read).  bf16: K pieces (one token x
+//    8 dims) t % 128 and t % 128 + 128; V dims 2p and 2p + 1 of tokens 8g ..
+//    8g + 7 (p = t % 64, g = t % 128 / 64).  fp8: the K piece (one token x 16
+//    dims) t % 128; V dims 2p, 2p + 1 of tokens 8g .. 8g + 7 (8 bytes each).
+template <int KIND, class Args>
+__device__ __forceinline__ void stage_load(const Args& a, const KeySrc& s, int32_t k0,
+                                           int32_t kend, Staged& R) {
+  const int th = threadIdx.x;
+  if constexpr (KIND == kCtxNhdFp8) {
+    const int r = th >> 3, j = th & 7;
+    const int32_t key = min(k0 + r, kend - 1);
+    int32_t blk = s.trow[key >> a.bs_log2];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const int64_t row = ((int64_t)blk * a.bs + (key & (a.bs - 1))) * a.Hkv + s.hkv;
+    R.k[0] = *(const u32x4_t*)(s.kb + row * kD + 16 * j);
+    R.v[0] = *(const u32x4_t*)(s.vb + row * kD + 16 * j);
+  } else {
+    const int b4 = th >> 7, i = th & 127;
+    const int32_t kb = k0 + 16 * b4;
+    int32_t blk = 0;
+    if (kb < kend) blk = s.trow[kb >> 4];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const int p = i & 63, g = i >> 6;
+    if constexpr (KIND == kCtxPreBf16) {
+      const int64_t base = ((int64_t)blk * a.Hkv + s.hkv) * 4096;
+      R.k[0] = *(const u32x4_t*)(s.kb + base + 16 * i);
+      R.k[1] = *(const u32x4_t*)(s.kb + base + 16 * (i + 128));
+      R.v[0] = *(const u32x4_t*)(s.vb + base + (g * 128 + 2 * p) * 16);
+      R.v[1] = *(const u32x4_t*)(s.vb + base + (g * 128 + 2 * p + 1) * 16);
+    } else {
+      const int64_t base = ((int64_t)blk * a.Hkv + s.hkv) * 2048;
+      R.k[0] = *(const u32x4_t*)(s.kb + base + 16 * i);
+      const u32x2_t v0 = *(const u32x2_t*)(s.vb + base + (2 * p) * 16 + 8 * g);
+      const u32x2_t v1 = *(const u32x2_t*)(s.vb + base + (2 * p + 1) * 16 + 8 * g);
+      R.v[0] = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// Decode this thread's share (loaded by stage_load) into the LDS rows of the
+// tile at k0 in `stage` (K rows kswz, V rows vswz, bf16).  Keys at or past
+// kend are stored as zeros (their scores are masked; their values must be
+// finite).
+template <int KIND>
+__device__ __forceinline__ void stage_store(const Staged& R, uint8_t* stage, int32_t k0,
+                                            int32_t kend) {
+  const int th = threadIdx.x;
+  uint8_t* kl = stage;
+  uint8_t* vl = stage + kKTile;
+  if constexpr (KIND == kCtxNhdFp8) {
+    const int r = th >> 3, j = th & 7;
+    *(bf16x8_t*)(kl + kswz(r, 2 * j)) = fp8x8_to_bf16(u32x2_t{R.k[0][0], R.k[0][1]});
+    *(bf16x8_t*)(kl + kswz(r, 2 * j + 1)) = fp8x8_to_bf16(u32x2_t{R.k[0][2], R.k[0][3]});
+    *(bf16x8_t*)(vl + vswz(r, 2 * j)) = fp8x8_to_bf16(u32x2_t{R.v[0][0], R.v[0][1]});
+    *(bf16x8_t*)(vl + vswz(r, 2 * j + 1)) = fp8x8_to_bf16(u32x2_t{R.v[0][2], R.v[0][3]});
+  } else {
+    const int b4 = th >> 7, i = th & 127;
+    const int p = i & 63, g = i >> 6;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    if constexpr (KIND == kCtxPreBf16) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int piece = i + 128 * u, row = 16 * b4 + (piece & 15);
+        *(u32x4_t*)(kl + kswz(row, piece >> 4)) = k0 + row < kend ? R.k[u] : zero;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 16 * b4 + 8 * g + j;
+        const uint32_t lo = (R.v[0][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        const uint32_t hi = (R.v[1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        *(uint32_t*)(vl + vswz(row, p >> 2) + 4 * (p & 3)) = k0 + row < kend ? (lo | (hi << 16)) : 0u;
+      }
+    } else {
+      const int row = 16 * b4 + (i & 15), c16 = i >> 4;
+      const bool ok = k0 + row < kend;
+      const bf16x8_t zb = {};
+      const bf16x8_t lo = fp8x8_to_bf16(u32x2_t{R.k[0][0], R.k[0][1]});
+      const bf16x8_t hi = fp8x8_to_bf16(u32x2_t{R.k[0][2], R.k[0][3]});
+      *(bf16x8_t*)(kl + kswz(row, 2 * c16)) = ok ? lo : zb;
+      *(bf16x8_t*)(kl + kswz(row, 2 * c16 + 1)) = ok ? hi : zb;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        // tokens 8g + 4 h2 .. + 3 of dims 2p (word h2) and 2p + 1 (word 2 + h2)
+        const f32x2_t d0a = __builtin_amdgcn_cvt_pk_f32_fp8((int)R.v[0][h2], false);
+        const f32x2_t d0b = __builtin_amdgcn_cvt_pk_f32_fp8((int)R.v[0][h2], true);
+        const f32x2_t d1a = __builtin_amdgcn_cvt_pk_f32_fp8((int)R.v[0][2 + h2], false);
+        const f32x2_t d1b = __builtin_amdgcn_cvt_pk_f32_fp8((int)R.v[0][2 + h2], true);
+        const uint32_t w[4] = {bf16_pair(d0a[0], d1a[0]), bf16_pair(d0a[1], d1a[1]),
+                               bf16_pair(d0b[0], d1b[0]), bf16_pair(d0b[1], d1b[1])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rw = 16 * b4 + 8 * g + 4 * h2 + e;
+          *(uint32_t*)(vl + vswz(rw, p >> 2) + 4 * (p & 3)) = k0 + rw < kend ? w[e] : 0u;
+        }
+      }
+    }
+  }
+}
+
 // Tile starting at key k0 (keys past k_end clamped to the last key) into the
 // stage at `stage`: wave w moves rows 8w..8w+7 of K and of V.  Whole tiles
 // whose wave rows are contiguous in memory (contiguous keys, or half of one
@@ -348,7 +477,7 @@ __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t 
 struct NoHooks {
   __device__ __forceinline__ void last(uint8_t*) const {}
 };
-template <bool PAGED, bool CAUSAL, int SB, class Hooks, class Args>
+template <bool PAGED, bool CAUSAL, int SB, class Hooks, class Args, int KIND = kCtxNhdBf16>
 __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const KeySrc& src,
                                          int32_t q0, int32_t q0_lo, int32_t k_begin, int32_t kend,
                                          int32_t n_tiles, int32_t blk_next, RowState& S,
@@ -358,6 +487,8 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
   const int32_t row = q0 + 32 * (wave & 3) + r; // this lane's query row (in sequence)
+  const float qk = KIND == kCtxNhdBf16 ? a.qk_mult : a.ctx_qk_mult;
+  const float vexp = a.ctx_vexp, linv = a.ctx_linv;
 
   // One key tile.  MASK = false for tiles that no row of the workgroup needs
   // masked (the whole tile is inside the key range and, for causal blocks,
@@ -381,9 +512,14 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
     constexpr bool LAST = decltype(last_tag)::value;
     const int32_t k0 = k_begin + t * kBN;
     uint8_t* st = smem + par * kStage;
+    Staged R;
     if constexpr (!LAST) {
-      dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend, blk_next);
-      if (t + 2 < n_tiles) blk_next = tile_block<PAGED>(a, src, k0 + 2 * kBN, kend);
+      if constexpr (KIND == kCtxNhdBf16) {
+        dma_tile<PAGED>(a, src, smem + (1 - par) * kStage, k0 + kBN, kend, blk_next);
+        if (t + 2 < n_tiles) blk_next = tile_block<PAGED>(a, src, k0 + 2 * kBN, kend);
+      } else {
+        stage_load<KIND>(a, src, k0 + kBN, kend, R);
+      }
     }
 
     // A diagonal tile whose first key lies past every row of this wave
@@ -419,7 +555,7 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[ks2][i]);
-      mt = xor32_max(mt) * a.qk_mult;                     // exp2 domain
+      mt = xor32_max(mt) * qk;                            // exp2 domain
       // Lazy rescale: the reference max only moves when some row's max grew by
       // more than 8, so probabilities stay <= 2^8 and most tiles skip the O^T
       // rescale.  Any reference works: numerator and denominator share it.
@@ -432,15 +568,19 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
         S.m_run = m_new;
       }
       const float m_use = (S.m_run == kNegInf) ? 0.f : S.m_run;
+      // fp8 context: p carries the factor v_scale (added to its exponent) so
+      // the products with the decoded codes are p * value; the row sum does not
       float psum = 0.f;
+      const float shift = KIND == kCtxNhdBf16 ? -m_use : vexp - m_use;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[ks2][i] = fast_exp2(__builtin_fmaf(s[ks2][i], a.qk_mult, -m_use));
+          s[ks2][i] = fast_exp2(__builtin_fmaf(s[ks2][i], qk, shift));
           psum += s[ks2][i];
         }
-      S.l_run += psum;
+      if constexpr (KIND == kCtxNhdBf16) S.l_run += psum;
+      else S.l_run = __builtin_fmaf(psum, linv, S.l_run);
 
       // P^T as B operand: k-step kk covers keys 16kk + {4hh..4hh+3, 8+4hh..8+4hh+3}
       bf16x8_t pb[4];
@@ -461,6 +601,8 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
       }
     }
 
+    if constexpr (KIND != kCtxNhdBf16 && !LAST)
+      stage_store<KIND>(R, smem + (1 - par) * kStage, k0 + kBN, kend);
     dma_wait_for(blk_next);
     __syncthreads();
   };
@@ -509,7 +651,7 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
 // q0_hi): copy the first tile, then the tile loop.  The LDS double buffer is
 // filled and drained inside, so phases with different sources can follow
 // each other.
-template <bool PAGED, bool CAUSAL, bool FIRST = false>
+template <bool PAGED, bool CAUSAL, bool FIRST = false, int KIND = kCtxNhdBf16>
 __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
                                          int32_t q0, int32_t q0_lo, int32_t q0_hi, int32_t qn,
                                          int32_t k_begin, int32_t k_end, RowState& S) {
@@ -523,9 +665,16 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
   const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
 
   if constexpr (!FIRST) __syncthreads();      // a previous phase may still read the buffers
-  dma_tile<PAGED>(a, src, smem, k_begin, kend, tile_block<PAGED>(a, src, k_begin, kend));
-  // table entry of the next tile's rows (the step copying tile t+1 looks up t+2)
-  int32_t blk_next = n_tiles > 1 ? tile_block<PAGED>(a, src, k_begin + kBN, kend) : 0;
+  int32_t blk_next = 0;
+  if constexpr (KIND == kCtxNhdBf16) {
+    dma_tile<PAGED>(a, src, smem, k_begin, kend, tile_block<PAGED>(a, src, k_begin, kend));
+    // table entry of the next tile's rows (the step copying tile t+1 looks up t+2)
+    blk_next = n_tiles > 1 ? tile_block<PAGED>(a, src, k_begin + kBN, kend) : 0;
+  } else {
+    Staged R;
+    stage_load<KIND>(a, src, k_begin, kend, R);
+    stage_store<KIND>(R, smem, k_begin, kend);
+  }
   dma_wait_for(blk_next);
   // Q^T was loaded before this wait; passing it through an empty asm tells the
   // compiler so.  Otherwise its wait insertion treats the Q loads as possibly
@@ -535,8 +684,8 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(S.qb[ks]));
   __syncthreads();
-  key_loop<PAGED, CAUSAL, 0>(a, smem, src, q0, q0_lo, k_begin, kend, n_tiles, blk_next, S,
-                            NoHooks{});
+  key_loop<PAGED, CAUSAL, 0, NoHooks, AttnArgs, KIND>(a, smem, src, q0, q0_lo, k_begin, kend,
+                                                     n_tiles, blk_next, S, NoHooks{});
 }
 
 // Write the rows of this block: bf16 output + lse, or an fp32 partial
@@ -831,6 +980,7 @@ void prefill_stream_kernel(AttnArgs) {
 // p >= 1: the new tokens against context chunk p-1 = cached tokens
 // [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
 // fp32 partial; extend_merge_kernel combines them.
+template <int KIND>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
@@ -857,8 +1007,8 @@ void extend_kernel(AttnArgs a) {
     const int32_t kb = (part - 1) * a.chunk_tokens;
     if (kb >= C) return;
     init_rows(a, rb.h, s0, rb.q0, qn, S);
-    run_keys<true, false, true>(a, smem, paged_keys(a, seq, hkv), rb.q0, rb.q0_lo, rb.q0_hi, qn, kb,
-                                min(C, kb + a.chunk_tokens), S);
+    run_keys<true, false, true, KIND>(a, smem, paged_keys(a, seq, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
+                                      qn, kb, min(C, kb + a.chunk_tokens), S);
   }
   finish_rows<true>(a, rb.h, s0, rb.q0, qn, part, S);
 }
@@ -875,6 +1025,7 @@ void extend_kernel(AttnArgs a) {
 // the same, without a pipeline restart per chunk.  Q comes in through the
 // per-wave LDS regions and the output leaves through them, as in the
 // persistent prefill.
+template <int KIND>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void extend_fused_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQArea + kWaves * kQRegion];
@@ -902,8 +1053,14 @@ void extend_fused_kernel(AttnArgs a) {
   dma_q(a, smem, it);
   int32_t blk1 = 0;
   if (C > 0) {
-    dma_tile<true>(a, ctx, smem, 0, C, tile_block<true>(a, ctx, 0, C));
-    blk1 = C > kBN ? tile_block<true>(a, ctx, kBN, C) : 0;
+    if constexpr (KIND == kCtxNhdBf16) {
+      dma_tile<true>(a, ctx, smem, 0, C, tile_block<true>(a, ctx, 0, C));
+      blk1 = C > kBN ? tile_block<true>(a, ctx, kBN, C) : 0;
+    } else {
+      Staged R;
+      stage_load<KIND>(a, ctx, 0, C, R);
+      stage_store<KIND>(R, smem, 0, C);
+    }
   } else {
     dma_tile<false>(a, fresh, smem, 0, kend, 0);
   }
@@ -914,7 +1071,8 @@ void extend_fused_kernel(AttnArgs a) {
   clear_rows(S);
   if (C > 0) {
     const int32_t nt = (C + kBN - 1) / kBN;
-    key_loop<true, false, 0>(a, smem, ctx, rb.q0, rb.q0_lo, 0, C, nt, blk1, S, NoHooks{});
+    key_loop<true, false, 0, NoHooks, AttnArgs, KIND>(a, smem, ctx, rb.q0, rb.q0_lo, 0, C, nt,
+                                                      blk1, S, NoHooks{});
     run_keys<false, true>(a, smem, fresh, rb.q0, rb.q0_lo, rb.q0_hi, qn, 0, qn, S);
   } else {
     const int32_t nt_new = (kend + kBN - 1) / kBN;
@@ -1077,18 +1235,35 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.chunk_tokens = p.chunk_tokens;
   a.rows = total_new;
   a.qk_mult = scale * kLog2e;
+  a.ctx_qk_mult = scale * c.k_scale * kLog2e;
+  a.ctx_vexp = __builtin_log2f(c.v_scale);
+  a.ctx_linv = 1.0f / c.v_scale;
   a.qt_major = n_qtiles <= 16 ? 1 : 0;
+  const int kind = c.layout == KV_LAYOUT_NHD ? (c.dtype == KV_DTYPE_BF16 ? kCtxNhdBf16 : kCtxNhdFp8)
+                                             : (c.dtype == KV_DTYPE_BF16 ? kCtxPreBf16 : kCtxPreFp8);
   if (p.fused) {
     a.items = (int64_t)num_seqs * a.Hkv * a.Gs;          // lanes
     a.grid_pad = work_grid(a.items, a.n_qitems);
     if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(extend_fused_kernel, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)a.grid_pad);
+    switch (kind) {
+      case kCtxNhdBf16: hipLaunchKernelGGL(extend_fused_kernel<kCtxNhdBf16>, grid, dim3(kThreads), 0, s, a); break;
+      case kCtxNhdFp8: hipLaunchKernelGGL(extend_fused_kernel<kCtxNhdFp8>, grid, dim3(kThreads), 0, s, a); break;
+      case kCtxPreBf16: hipLaunchKernelGGL(extend_fused_kernel<kCtxPreBf16>, grid, dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL(extend_fused_kernel<kCtxPreFp8>, grid, dim3(kThreads), 0, s, a); break;
+    }
     return hipGetLastError();
   }
   a.items = (int64_t)num_seqs * p.n_parts * a.Hkv * a.Gs;  // lanes
   a.grid_pad = work_grid(a.items, a.n_qitems);
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(extend_kernel, dim3((unsigned)a.grid_pad), dim3(kThreads), 0, s, a);
+  const dim3 grid((unsigned)a.grid_pad);
+  switch (kind) {
+    case kCtxNhdBf16: hipLaunchKernelGGL(extend_kernel<kCtxNhdBf16>, grid, dim3(kThreads), 0, s, a); break;
+    case kCtxNhdFp8: hipLaunchKernelGGL(extend_kernel<kCtxNhdFp8>, grid, dim3(kThreads), 0, s, a); break;
+    case kCtxPreBf16: hipLaunchKernelGGL(extend_kernel<kCtxPreBf16>, grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(extend_kernel<kCtxPreFp8>, grid, dim3(kThreads), 0, s, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rh = (int64_t)total_new * num_q_heads;

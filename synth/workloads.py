@@ -348,10 +348,10 @@ class MixedBatch:
 
 
 def mixed_batch(seed, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                dec_lens, ext_ctx, ext_new, pre_lens) -> MixedBatch:
+                dec_lens, ext_ctx, ext_new, pre_lens, layout="nhd", dtype="bf16") -> MixedBatch:
     """Build a reordered mixed batch from explicit per-request sizes."""
     rng = np.random.default_rng(seed)
-    spec = CacheSpec(num_blocks, block_size, num_kv_heads, head_dim)
+    spec = CacheSpec(num_blocks, block_size, num_kv_heads, head_dim, layout, dtype)
     dec_lens = np.asarray(dec_lens, dtype=np.int32)
     ext_ctx = np.asarray(ext_ctx, dtype=np.int32)
     ext_new = np.asarray(ext_new, dtype=np.int32)
@@ -403,3 +403,26 @@ def long_context_extend(seed=4, n_seq=2, ctx=100000, new=8192, num_blocks=16384)
     """2 requests with 100000 cached tokens and 8192 new tokens each; 64:8
     heads, D 128, bf16, block 16 (an extend-only batch)."""
     return mixed_batch(seed, 64, 8, 128, 16, num_blocks, [], [ctx] * n_seq, [new] * n_seq, [])
+
+
+def heavy_tailed_mixed_batch(seed=6, n_decode=64, n_extend=12, n_prefill=2,
+                             num_blocks=20480) -> MixedBatch:
+    """A serving batch with heavy-tailed lengths (prefix-cache hits and
+    multi-turn requests: many short extends beside a few long ones), 64:4
+    heads, D 128, bf16, block 16, reordered [decode:extend:prefill].
+    Lengths are lognormal, rounded and clipped:
+      decode contexts   median 2000, sigma 1.0, in [16, 32768]
+      extend new tokens median 96,   sigma 1.3, in [2, 4096]
+      extend contexts   median 3000, sigma 1.0, in [16, 32768]
+      prefill lengths   median 1500, sigma 0.8, in [64, 8192]"""
+    rng = np.random.default_rng(seed + 11)
+
+    def lengths(n, median, sigma, lo, hi):
+        x = rng.lognormal(np.log(median), sigma, size=n)
+        return np.clip(np.rint(x), lo, hi).astype(np.int32)
+
+    dec = lengths(n_decode, 2000, 1.0, 16, 32768)
+    ext_new = lengths(n_extend, 96, 1.3, 2, 4096)
+    ext_ctx = lengths(n_extend, 3000, 1.0, 16, 32768)
+    pre = lengths(n_prefill, 1500, 0.8, 64, 8192)
+    return mixed_batch(seed, 64, 4, 128, 16, num_blocks, dec, ext_ctx, ext_new, pre)
