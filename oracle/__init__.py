@@ -33,6 +33,9 @@ cache      paged cache model: gather through the block table (both layouts),
 attention  exact softmax attention for the decode, prefill and extend paths.
 merge      log-sum-exp merge of partial attention states.
 batch      request classification and [decode:extend:prefill] reorder.
+mla        absorbed multi-head latent attention decode over a paged 576-dim
+           latent cache ("Beyond just running ...", section "AITER MLA
+           backend: optimised for DeepSeek").
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``
 (closed forms, invariants, library routines, brute force and the pages'

@@ -426,3 +426,46 @@ def heavy_tailed_mixed_batch(seed=6, n_decode=64, n_extend=12, n_prefill=2,
     ext_ctx = lengths(n_extend, 3000, 1.0, 16, 32768)
     pre = lengths(n_prefill, 1500, 0.8, 64, 8192)
     return mixed_batch(seed, 64, 4, 128, 16, num_blocks, dec, ext_ctx, ext_new, pre)
+
+
+# ----------------------------------------------------------------------------
+# MLA (absorbed latent) decode
+# ----------------------------------------------------------------------------
+@dataclass
+class MlaDecode:
+    cache: np.ndarray         # [num_blocks, block_size, 576] bf16 bits
+    q: np.ndarray             # [B, H, 576] bf16 bits (absorbed queries)
+    block_tables: np.ndarray  # [B, max_blocks] int32
+    seq_lens: np.ndarray      # [B] int32
+    block_size: int
+    scale: float
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def num_heads(self) -> int:
+        return self.q.shape[1]
+
+
+def mla_decode_workload(seed, batch, num_heads, block_size, num_blocks, len_lo, len_hi,
+                        fixed_lens=None, latent=576) -> MlaDecode:
+    """Latent rows and absorbed queries N(0,1) in bf16; fully fragmented
+    tables (the last block is the poison block); scale 1/sqrt(576)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(len_lo, len_hi + 1, size=batch).astype(np.int32)
+    if fixed_lens is not None:
+        lens[:len(fixed_lens)] = fixed_lens
+    tables = block_tables_for(rng, lens, block_size, num_blocks)
+    cache = normal_bf16(rng, (num_blocks, block_size, latent))
+    q = normal_bf16(rng, (batch, num_heads, latent))
+    return MlaDecode(cache, q, tables, lens, block_size, float(1.0 / np.sqrt(latent)))
+
+
+def deepseek_mla_decode(seed=7, batch=128, len_lo=10000, len_hi=11000,
+                        num_blocks=90112) -> MlaDecode:
+    """One GPU's share of DeepSeek-R1 MLA decode under TP8: 16 of the 128
+    query heads over the (replicated) 576-dim latent cache, block 16, batch
+    128 at ISL 10K + up to 1K generated tokens."""
+    return mla_decode_workload(seed, batch, 16, 16, num_blocks, len_lo, len_hi)
