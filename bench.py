@@ -35,6 +35,9 @@ over one batch of seeded synthetic input that is already resident in HBM:
       Step = kv_write + paged_decode + extend_attn + prefill_attn (three-way
       routing); the same batch as ONE extend_attn call over every request is
       timed beside it.
+  deepseek_mla_decode: one GPU's share of DeepSeek-R1 MLA decode under TP8 --
+      batch 128, 16 query heads, 576-dim bf16 latent rows, block 16, context
+      [10000, 11000].  Step = mla_decode.
 The default run measures the headline and then every other workload as a
 "secondary" entry, each with its roofline and its CPU-oracle baseline.
 
@@ -633,6 +636,44 @@ def build_heavy_tailed_mixed_batch(torch, pk, w, dev):
     return calls, "extend_attn", "mfma", config, cpu_sample, ("tokens/s", T), [unified]
 
 
+def build_deepseek_mla_decode(torch, pk, w, dev):
+    st = w.deepseek_mla_decode()
+    cache, q = dev(st.cache), dev(st.q)
+    tables, lens = dev(st.block_tables), dev(st.seq_lens)
+    msl = int(st.seq_lens.max())
+    B, H = st.batch, st.num_heads
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(int(pk.lib().mla_decode_workspace_bytes(B, H, msl)), 16),
+                     dtype=torch.uint8, device=q.device)
+    tok = float(st.seq_lens.astype(np.int64).sum())
+    blocks = float(((st.seq_lens + 15) // 16).sum())
+    mla_bytes = tok * 576 * 2 + B * H * (576 + 512) * 2 + B * H * 4 + blocks * 4 + B * 4
+    mla_flops = tok * H * 2 * (576 + 512)
+    calls = [Call("mla_decode", lambda: pk.mla_decode(cache, q, tables, lens, msl, st.scale,
+                                                      out=out, lse=lse, workspace=ws),
+                  mla_bytes, mla_flops)]
+    config = {"workload": "deepseek-r1 MLA absorbed decode, one GPU's share under TP8: batch 128, "
+                          "16 query heads, 576-dim bf16 latent rows (value = first 512), block 16, "
+                          "ctx U[10000,11000]",
+              "batch": B, "num_heads": H, "kv_tokens": int(tok)}
+
+    def cpu_sample(budget_s):
+        from oracle import bf16 as ob, mla
+        qf = ob.to_f64(st.q)
+        t0, done, n = time.perf_counter(), 0.0, 0
+        while time.perf_counter() - t0 < budget_s:
+            b = n % B
+            mla.mla_decode(qf[b:b + 1], st.cache, st.block_tables[b:b + 1], st.seq_lens[b:b + 1],
+                           st.scale, 16)
+            done += float(st.seq_lens[b]) * 576 * 2
+            n += 1
+        dt = time.perf_counter() - t0
+        return done / dt / 1e9, f"oracle MLA decode of {n} requests of this batch; {dt:.1f} s"
+
+    return calls, "mla_decode", "hbm", config, cpu_sample, ("GB/s", None)
+
+
 WORKLOADS = {
     "llama70b_decode_layer": build_llama70b_decode_layer,
     "qwen3_mixed_batch": build_qwen3_mixed_batch,
@@ -641,6 +682,7 @@ WORKLOADS = {
     "tiny_decode": build_tiny_decode,
     "decode_layout_compare": build_decode_layout_compare,
     "heavy_tailed_mixed_batch": build_heavy_tailed_mixed_batch,
+    "deepseek_mla_decode": build_deepseek_mla_decode,
 }
 SECONDARY_METRIC = {
     "qwen3_mixed_batch": "mixed-batch attention tokens/s",
@@ -650,6 +692,7 @@ SECONDARY_METRIC = {
     "decode_layout_compare": "paged decode HBM GB/s, bf16 preshuffled vs NHD layout",
     "heavy_tailed_mixed_batch": "mixed-batch attention tokens/s, heavy-tailed lengths, "
                                 "three-way routed vs one unified extend call",
+    "deepseek_mla_decode": "MLA absorbed decode HBM GB/s (576-dim latent cache)",
 }
 
 
@@ -746,7 +789,7 @@ def main():
             if c.flops:
                 d["TFLOP/s"] = round(c.flops / (avg * 1e-3) / 1e12, 1)
                 d["mfma_frac"] = round(d["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)
-            if c.name.startswith("paged_decode"):
+            if c.name.startswith("paged_decode") or c.name == "mla_decode":
                 cold = timed(c, True)
                 d["ms_cold"] = round(cold, 5)
                 d["GB/s_cold"] = round(c.bytes / (cold * 1e-3) / 1e9, 1)

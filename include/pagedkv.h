@@ -13,6 +13,8 @@
  *   prefill_attn     causal attention over fresh prompts (varlen batch)
  *   kv_pack_layer    gather one layer's KV blocks into a contiguous buffer
  *   kv_unpack_layer  scatter such a buffer into (other) blocks of a cache
+ *   mla_decode       absorbed multi-head latent attention decode over a paged
+ *                    576-dim latent cache
  *
  * Sources (web pages; cited by title and section):
  *  [ROCm]  "Beyond just running: native inference optimisation in vLLM on AMD
@@ -272,6 +274,35 @@ int extend_attn_ex(const kv_cache_t* cache, const void* q, const void* k_new,
                    int32_t max_ctx_len, int32_t num_q_heads, int32_t chunk_budget_tokens,
                    float scale, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, int32_t mode, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mla_decode -- [ROCm] section "AITER MLA backend: optimised for DeepSeek":
+ * multi-head latent attention keeps one 576-dim latent row per token (about
+ * 14x less than standard MHA) shared by every query head, and decodes
+ * "absorbed", directly in that latent space; decode stays bound by memory
+ * bandwidth.  The benchmark there runs with block size 16.
+ *   kv_cache      [num_blocks][block_size][576] bf16: row = [c (512) | k_rope (64)]
+ *   kv_dim, v_dim 576 and 512 (the only supported values): the score of
+ *                 head h against token j is scale * <q_h, row_j> over all 576
+ *                 dims, the value is the row's first 512 dims (the compressed
+ *                 KV; the split is a reading of DeepSeek's published MLA)
+ *   q             [batch][num_heads][576] bf16 (absorbed queries)
+ *   block_tables  [batch][max_blocks_per_seq] int32
+ *   seq_lens      [batch] int32 in [0, max_seq_len]; 0 gives out = 0, lse = -inf
+ *   block_size    power of two in [16, 256]
+ *   scale         finite and > 0
+ *   out           [batch][num_heads][512] bf16 (the latent output; its
+ *                 up-projection is part of the model, not of attention)
+ *   lse           [batch][num_heads] fp32 or NULL
+ *   workspace     >= mla_decode_workspace_bytes(...) bytes (plan + partials)
+ * Balanced split-K over the concatenated token stream, as paged_decode.
+ * ------------------------------------------------------------------------- */
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len);
+int mla_decode(const void* kv_cache, int32_t num_blocks, int32_t block_size, int32_t kv_dim,
+               int32_t v_dim, const void* q, int32_t batch, int32_t num_heads,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out,
+               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Layer pack / unpack -- [PD] section "Architecture", write mode: after each

@@ -7,8 +7,9 @@ HIP stream.  The binding refuses to run when the library has not been built;
 there is no fallback implementation.
 
 Calls (same names as the C ABI):
-    kv_write, paged_decode, prefill_attn, extend_attn,
-    kv_layer_packed_bytes, kv_pack_layer, kv_unpack_layer, reorder_batch
+    kv_write, paged_decode, paged_decode_noalloc, prefill_attn, extend_attn,
+    mla_decode, kv_layer_packed_bytes, kv_pack_layer, kv_unpack_layer,
+    reorder_batch
 """
 from __future__ import annotations
 
@@ -60,6 +61,9 @@ _SIGS = {
     "extend_attn_workspace_bytes_ex": (_SZ, [_PC, _I32, _I32, _I32, _I32, _I32, _I32]),
     "extend_attn_ex": (ctypes.c_int, [_PC, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                       _I32, _I32, _F, _P, _P, _P, _SZ, _I32, _P]),
+    "mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_decode": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P, _I32, _P, _I32, _F,
+                                  _P, _P, _P, _SZ, _P]),
     "kv_layer_packed_bytes": (_SZ, [_PC, _I32]),
     "kv_pack_layer": (ctypes.c_int, [_PC, _P, _I32, _P, _SZ, _P]),
     "kv_unpack_layer": (ctypes.c_int, [_PC, _P, _I32, _P, _SZ, _P]),
@@ -312,6 +316,38 @@ def extend_attn(cache: PagedKVCache, q, k_new, v_new, cu_q_lens, ctx_lens, block
                                 float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                 int(workspace.numel() * workspace.element_size()),
                                 _EXTEND_MODES[mode], _stream(q)))
+    return out, lse
+
+
+def mla_decode(kv_cache, q, block_tables, seq_lens, max_seq_len: int, scale: float,
+               out=None, lse=None, workspace=None):
+    """Absorbed MLA decode: kv_cache [num_blocks, block_size, 576] bf16 latent
+    rows, q [B, H, 576] bf16 -> (out [B, H, 512] bf16, lse [B, H] fp32)."""
+    import torch
+    _want(kv_cache, "kv_cache", (torch.bfloat16,), 3)
+    _want(q, "q", (torch.bfloat16,), 3)
+    _want(block_tables, "block_tables", (torch.int32,), 2)
+    _want(seq_lens, "seq_lens", (torch.int32,), 1)
+    _want(out, "out", (torch.bfloat16,), 3, optional=True)
+    _want(lse, "lse", (torch.float32,), 2, optional=True)
+    _want(workspace, "workspace", (torch.uint8,), 1, optional=True)
+    B, H, Dk = q.shape
+    if block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_tables / seq_lens must have one row per request")
+    _on_gpu(kv_cache=kv_cache, q=q, block_tables=block_tables, seq_lens=seq_lens, out=out,
+            lse=lse, workspace=workspace)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = int(lib().mla_decode_workspace_bytes(B, H, int(max_seq_len)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().mla_decode(_ptr(kv_cache), int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+                            int(kv_cache.shape[2]), 512, _ptr(q), B, H, _ptr(block_tables),
+                            int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                            float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                            int(workspace.numel()), _stream(q)))
     return out, lse
 
 

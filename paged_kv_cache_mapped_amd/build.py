@@ -27,7 +27,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["kv_write.hip", "kv_pack.hip", "paged_decode.hip", "flash_attn.hip", "capi.cpp"]
+SOURCES = ["kv_write.hip", "kv_pack.hip", "paged_decode.hip", "flash_attn.hip", "mla_decode.hip",
+           "capi.cpp"]
 
 
 def _hipcc() -> str:

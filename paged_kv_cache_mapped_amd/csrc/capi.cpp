@@ -325,6 +325,66 @@ int extend_attn(const kv_cache_t* cache, const void* q, const void* k_new, const
                         KV_EXTEND_AUTO, stream);
 }
 
+static int mla_checks(int32_t num_blocks, int32_t block_size, int32_t kv_dim, int32_t v_dim,
+                      int32_t batch, int32_t num_heads, int32_t max_seq_len, const char* fn) {
+  if (kv_dim != 576 || v_dim != 512)
+    return fail(KV_ENOTSUP, "%s: latent rows of 576 dims with a 512-dim value part only (got %d, %d)",
+                fn, kv_dim, v_dim);
+  if (num_blocks <= 0) return fail(KV_EINVAL, "%s: num_blocks must be > 0", fn);
+  if (!pow2(block_size) || block_size > 256)
+    return fail(KV_EINVAL, "%s: block_size %d must be a power of two in [1, 256]", fn, block_size);
+  if (block_size < 16)
+    return fail(KV_ENOTSUP, "%s: block_size %d below the 16-token tile", fn, block_size);
+  if (batch <= 0 || batch > 65535) return fail(KV_EINVAL, "%s: batch must be in [1, 65535]", fn);
+  if (num_heads <= 0 || num_heads > 4096) return fail(KV_EINVAL, "%s: num_heads must be in [1, 4096]", fn);
+  if (max_seq_len <= 0) return fail(KV_EINVAL, "%s: max_seq_len must be > 0", fn);
+  if ((int64_t)batch * (((int64_t)max_seq_len + 15) & ~(int64_t)15) >= ((int64_t)1 << 31))
+    return fail(KV_EINVAL, "%s: batch * max_seq_len must stay below 2^31", fn);
+  if ((int64_t)num_blocks * block_size * 1152 > ((int64_t)1 << 46))
+    return fail(KV_EINVAL, "%s: cache larger than 64 TiB", fn);
+  return KV_OK;
+}
+
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t max_seq_len) {
+  if (mla_checks(1, 16, 576, 512, batch, num_heads, max_seq_len, "mla_decode_workspace_bytes"))
+    return 0;
+  const pkv::MlaPlan p = pkv::plan_mla(batch, num_heads, max_seq_len, nullptr);
+  return pkv::mla_workspace_bytes(p, batch, num_heads);
+}
+
+int mla_decode(const void* kv_cache, int32_t num_blocks, int32_t block_size, int32_t kv_dim,
+               int32_t v_dim, const void* q, int32_t batch, int32_t num_heads,
+               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+               int32_t max_seq_len, float scale, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const char* fn = "mla_decode";
+  int st = mla_checks(num_blocks, block_size, kv_dim, v_dim, batch, num_heads, max_seq_len, fn);
+  if (st) return st;
+  if (!kv_cache || !q || !block_tables || !seq_lens || !out)
+    return fail(KV_EINVAL, "%s: kv_cache, q, block_tables, seq_lens and out must be non-NULL", fn);
+  if (!aligned16(kv_cache) || !aligned16(q) || !aligned16(out))
+    return fail(KV_EINVAL, "%s: kv_cache, q and out must be 16-byte aligned", fn);
+  if (max_blocks_per_seq <= 0) return fail(KV_EINVAL, "%s: max_blocks_per_seq must be > 0", fn);
+  if ((int64_t)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(KV_EINVAL, "%s: max_seq_len %d exceeds the table capacity %lld", fn, max_seq_len,
+                (long long)max_blocks_per_seq * block_size);
+  if ((int64_t)max_blocks_per_seq * block_size > (int64_t)1 << 30)
+    return fail(KV_EINVAL, "%s: table capacity above 2^30 tokens", fn);
+  st = check_scale(scale, fn);
+  if (st) return st;
+  const pkv::MlaPlan p = pkv::plan_mla(batch, num_heads, max_seq_len, (hipStream_t)stream);
+  const size_t need = pkv::mla_workspace_bytes(p, batch, num_heads);
+  if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (workspace_bytes < need)
+    return fail(KV_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(KV_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  return hip_status(pkv::launch_mla_decode(p, kv_cache, num_blocks, block_size, q, batch,
+                                           num_heads, block_tables, max_blocks_per_seq, seq_lens,
+                                           max_seq_len, scale, out, lse, workspace,
+                                           (hipStream_t)stream),
+                    fn);
+}
+
 size_t kv_layer_packed_bytes(const kv_cache_t* cache, int32_t n) {
   if (check_cache(cache, "kv_layer_packed_bytes") || n < 0) return 0;
   return (size_t)2 * n * cache->block_size * cache->num_kv_heads * cache->head_dim * elem_bytes(cache);

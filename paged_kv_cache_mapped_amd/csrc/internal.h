@@ -59,6 +59,23 @@ hipError_t launch_decode(const kv_cache_t& c, const DecodePlan& p, const void* q
                          int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
                          float scale, void* out, float* lse, void* workspace, hipStream_t s);
 
+// ----------------------------------------------------------------- MLA decode
+struct MlaPlan {
+  int32_t n_gchunks;         // groups of up to 16 query heads
+  int32_t waves;             // workers (4 per compute unit)
+  int32_t target_pieces;     // pieces the automatic length aims at
+  int32_t len_min, len_max;  // bounds of the piece length (tokens, multiple of 16)
+  int32_t max_pieces;        // upper bound of the number of pieces
+  int32_t part_rows;         // partial rows per head: max_pieces + batch
+};
+MlaPlan plan_mla(int32_t batch, int32_t num_heads, int32_t max_seq_len, hipStream_t stream);
+size_t mla_workspace_bytes(const MlaPlan& p, int32_t batch, int32_t num_heads);
+hipError_t launch_mla_decode(const MlaPlan& p, const void* cache, int32_t num_blocks,
+                             int32_t block_size, const void* q, int32_t batch, int32_t num_heads,
+                             const int32_t* tables, int32_t max_blocks, const int32_t* seq_lens,
+                             int32_t max_seq_len, float scale, void* out, float* lse,
+                             void* workspace, hipStream_t s);
+
 // ----------------------------------------------------------------- prefill / extend
 hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           const int32_t* cu_seqlens, int32_t num_seqs, int32_t max_seqlen,
