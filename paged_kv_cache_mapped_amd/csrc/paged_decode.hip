@@ -148,24 +148,43 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
       }
     }
   }
-  // V: NHD rows as 16-byte chunks of whole rows (row 4*j4 + lane/16, chunk
-  // lane%16); preshuffled V as the V^T operand (8 tokens of dim 16n + r).
+  // V: NHD rows as 16-byte chunks of whole rows (bf16: row 4*j4 + lane/16,
+  // chunk lane%16; fp8: row 8*j + lane/8, chunk lane%8); preshuffled V as the
+  // V^T operand (bf16: 8 tokens of dim 16n + r; fp8: see below).
   if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-    const int a4 = lane >> 4, c16 = lane & 15;
+    if constexpr (DT == KV_DTYPE_BF16) {
+      const int a4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int j4 = 0; j4 < 8; ++j4) {
-      const int32_t tok = min(t0 + 4 * j4 + a4, t_end - 1);
-      const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
-      const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
-      if constexpr (DT == KV_DTYPE_BF16) {
+      for (int j4 = 0; j4 < 8; ++j4) {
+        const int32_t tok = min(t0 + 4 * j4 + a4, t_end - 1);
+        const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+        const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
         R.v[j4] = *(const u32x4_t*)(a.vc + row * (kD * 2) + c16 * 16);
-      } else {
-        const u32x2_t c = *(const u32x2_t*)(a.vc + row * kD + c16 * 8);
-        R.v[j4] = u32x4_t{c[0], c[1], 0u, 0u};
+      }
+    } else {
+      const int a8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int32_t tok = min(t0 + 8 * j + a8, t_end - 1);
+        const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+        const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
+        R.v[j] = *(const u32x4_t*)(a.vc + row * kD + c8 * 16);
       }
     }
+  } else if constexpr (DT == KV_DTYPE_FP8_E4M3) {
+    // 16-byte loads: lane (q4, r), load j takes the 16 tokens of block half
+    // q4 / 2 of the tile for dim 16 (2 j + q4 % 2) + r; consume_tile trades
+    // halves between lanes q4 and q4 ^ 1 so that each ends with tokens
+    // 8 q4 .. 8 q4 + 7 of dims 16 (2 j) + r and 16 (2 j + 1) + r.
+    const int32_t tb = min(t0 + 16 * (q4 >> 1), (t_end - 1) & ~15);   // aligned to 16
+    const int32_t blk = s_tab[(tb >> a.bs_log2) - ib0];
+    const int32_t off = tb & (a.bs - 1);
+    const int64_t base = (((int64_t)blk * a.Hkv + hkv) * (a.bs / 16) + off / 16) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      R.v[j] = *(const u32x4_t*)(a.vc + (base + 16 * (2 * j + (q4 & 1)) + r) * 16);
   } else {
-    constexpr int X = (DT == KV_DTYPE_BF16) ? 8 : 16;
+    constexpr int X = 8;                                        // bf16
     const int32_t tb = min(t0 + 8 * q4, (t_end - 1) & ~7);   // 8 tokens, aligned to 8
     const int32_t blk = s_tab[(tb >> a.bs_log2) - ib0];
     const int32_t off = tb & (a.bs - 1);
@@ -173,12 +192,7 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int64_t e = (base + 16 * n + r) * X + (off % X);
-      if constexpr (DT == KV_DTYPE_BF16) {
-        R.v[n] = *(const u32x4_t*)(a.vc + e * 2);
-      } else {
-        const u32x2_t c = *(const u32x2_t*)(a.vc + e);
-        R.v[n] = u32x4_t{c[0], c[1], 0u, 0u};
-      }
+      R.v[n] = *(const u32x4_t*)(a.vc + e * 2);
     }
   }
 }
@@ -213,19 +227,40 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
   }
   bf16x8_t va[8];
   if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-    const int a4 = lane >> 4, c16 = lane & 15;
+    if constexpr (DT == KV_DTYPE_BF16) {
+      const int a4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int j4 = 0; j4 < 8; ++j4) {
-      u32x4_t w = R.v[j4];
-      if constexpr (DT != KV_DTYPE_BF16)
-        w = __builtin_bit_cast(u32x4_t, fp8x8_to_bf16(u32x2_t{w[0], w[1]}));
-      *(u32x4_t*)(vt + (4 * j4 + a4) * kVRowBytes + c16 * 16) = w;
+      for (int j4 = 0; j4 < 8; ++j4)
+        *(u32x4_t*)(vt + (4 * j4 + a4) * kVRowBytes + c16 * 16) = R.v[j4];
+    } else {
+      const int a8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t w = R.v[j];
+        uint8_t* dst = vt + (8 * j + a8) * kVRowBytes + c8 * 32;
+        *(bf16x8_t*)dst = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
+        *(bf16x8_t*)(dst + 16) = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+      }
     }
   } else {
+    if constexpr (DT == KV_DTYPE_BF16) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      if constexpr (DT == KV_DTYPE_BF16) va[n] = __builtin_bit_cast(bf16x8_t, R.v[n]);
-      else va[n] = fp8x8_to_bf16(u32x2_t{R.v[n][0], R.v[n][1]});
+      for (int n = 0; n < 8; ++n) va[n] = __builtin_bit_cast(bf16x8_t, R.v[n]);
+    } else {
+      // Load j of lane (q4, r) holds tokens [lo | hi] = [16 (q4/2) .. +7 |
+      // +8 .. +15] of dim 16 (2 j + q4 % 2) + r.  Swapping lo of the odd rows
+      // of 16 lanes with hi of the even rows leaves, in every lane, lo = dim
+      // 16 (2 j) + r and hi = dim 16 (2 j + 1) + r, both for tokens
+      // 8 q4 .. 8 q4 + 7 (v_permlane16_swap_b32: odd rows of the first
+      // operand <-> even rows of the second).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t l0 = R.v[j][0], l1 = R.v[j][1], h0 = R.v[j][2], h1 = R.v[j][3];
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+                     : "+v"(l0), "+v"(h0), "+v"(l1), "+v"(h1));
+        va[2 * j] = fp8x8_to_bf16(u32x2_t{l0, l1});
+        va[2 * j + 1] = fp8x8_to_bf16(u32x2_t{h0, h1});
+      }
     }
     if (partial) {
       const int32_t tv = t0 + 8 * q4;
