@@ -86,6 +86,7 @@ KERNEL_SOURCES = {
     "paged_decode": ["paged_decode.hip", "common.h"],
     "prefill_attn": ["flash_attn.hip", "common.h"],
     "extend_attn": ["flash_attn.hip", "common.h"],
+    "mla_decode": ["mla_decode.hip", "common.h"],
 }
 
 
