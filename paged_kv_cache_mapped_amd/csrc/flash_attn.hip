@@ -84,7 +84,8 @@ struct AttnArgs {
   int32_t n_qitems;         // query items per lane: 128-row tiles (pairs) or tile pairs
   int64_t items;            // lanes (work items = lanes x query items)
   int64_t grid_pad;         // launched workgroups (multiple of 8)
-  int32_t qt_major;         // work order inside an XCD's block of lanes
+  int32_t qt_major;         // work order inside an XCD's share of lanes
+  int32_t lchunk;           // lanes kept together on one XCD (query heads sharing a KV head)
   float qk_mult;            // scale * log2(e)
   // context scores and values of an fp8 cache: code * k_scale, code * v_scale
   float ctx_qk_mult;        // scale * k_scale * log2(e)
@@ -99,14 +100,19 @@ struct AttnArgs {
 // rows when the group size is even, else two consecutive query tiles of one
 // head.
 // Launched workgroup L runs on XCD L % 8, and the hardware hands workgroups
-// out in launch order as CUs free up.  XCD x owns the contiguous block of
-// lanes [x*hx, (x+1)*hx), so heads sharing a KV head (and its K/V tiles) share
-// that XCD's L2.  Inside the block the order is either query-tile-major with
+// out in launch order as CUs free up.  Lanes are dealt to the XCDs in chunks
+// of lchunk consecutive lanes (half the query-head pairs of one KV head): the
+// heads of a chunk share its K/V tiles in that XCD's L2, and the lanes of one
+// request -- 2 * H_kv chunks -- are spread over the XCDs, so a request that
+// is much longer than the others (a heavy-tailed batch) is worked on by the
+// whole GPU rather than by one or two XCDs.  Inside an XCD's share the order
+// is either query-tile-major with
 // the last query tiles (the heaviest under a causal mask) first, so the
 // in-order hand-out is a longest-first schedule (causal prefill, short
 // extends), or lane-major (a lane's tiles back to back, last first), which
 // keeps the workgroups of an XCD on fewer K/V streams when every tile costs
-// about the same (long non-causal work).  grid_pad = 8 * hx * n_qitems.
+// about the same (long non-causal work).  grid_pad = 8 * hx * n_qitems, hx a
+// multiple of lchunk.
 struct WorkItem {
   int64_t lane;
   int32_t qi;
@@ -116,17 +122,21 @@ __device__ __forceinline__ WorkItem work_item(const Args& a, int64_t L) {
   const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qitems);
   const int64_t j = L >> 3;
   WorkItem w;
+  int64_t l;                    // this XCD's l-th lane
   if (a.qt_major) {
     w.qi = a.n_qitems - 1 - (int32_t)(j / hx);
-    w.lane = (L & 7) * hx + j % hx;
+    l = j % hx;
   } else {
     w.qi = a.n_qitems - 1 - (int32_t)(j % a.n_qitems);
-    w.lane = (L & 7) * hx + j / a.n_qitems;
+    l = j / a.n_qitems;
   }
+  // chunks of lchunk consecutive lanes are dealt to the XCDs in turn
+  const int64_t c = a.lchunk;
+  w.lane = ((l / c) * 8 + (L & 7)) * c + l % c;
   return w;
 }
-static int64_t work_grid(int64_t lanes, int32_t n_qitems) {
-  return 8 * ((lanes + 7) / 8) * (int64_t)n_qitems;
+static int64_t work_grid(int64_t lanes, int32_t n_qitems, int32_t lchunk) {
+  return 8 * (((lanes + 8 * lchunk - 1) / (8 * lchunk)) * lchunk) * (int64_t)n_qitems;
 }
 // Persistent walk: the launched grid holds one workgroup per CU (a multiple of
 // 8); launched workgroup b runs the virtual workgroups 8m + (b & 7) of its
@@ -1132,6 +1142,7 @@ static void set_pairing(AttnArgs& a, int32_t n_qtiles) {
   a.pairs = (a.G % 2 == 0) ? 1 : 0;
   a.Gs = a.pairs ? a.G / 2 : a.G;
   a.n_qitems = a.pairs ? n_qtiles : (n_qtiles + 1) / 2;
+  a.lchunk = a.Gs >= 2 ? a.Gs / 2 : 1;
 }
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -1154,7 +1165,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.n_parts = 1;
   a.qk_mult = scale * kLog2e;
   a.items = (int64_t)num_seqs * num_kv_heads * a.Gs;     // lanes
-  a.grid_pad = work_grid(a.items, a.n_qitems);
+  a.grid_pad = work_grid(a.items, a.n_qitems, a.lchunk);
   a.qt_major = causal ? 1 : 0;
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(persistent_grid(a.grid_pad, s));
@@ -1243,7 +1254,7 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
                                              : (c.dtype == KV_DTYPE_BF16 ? kCtxPreBf16 : kCtxPreFp8);
   if (p.fused) {
     a.items = (int64_t)num_seqs * a.Hkv * a.Gs;          // lanes
-    a.grid_pad = work_grid(a.items, a.n_qitems);
+    a.grid_pad = work_grid(a.items, a.n_qitems, a.lchunk);
     if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.grid_pad);
     switch (kind) {
@@ -1255,7 +1266,7 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
     return hipGetLastError();
   }
   a.items = (int64_t)num_seqs * p.n_parts * a.Hkv * a.Gs;  // lanes
-  a.grid_pad = work_grid(a.items, a.n_qitems);
+  a.grid_pad = work_grid(a.items, a.n_qitems, a.lchunk);
   if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)a.grid_pad);
   switch (kind) {
