@@ -339,17 +339,41 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a) {
   const int32_t n_b = (cb + L - 1) / len - cb / len + 1;
   if (n_b <= 1) return;                        // written by the main pass
   const int64_t row0 = (int64_t)(cb / len + b) * a.H + h;
+  // chunks of 8 partials, every load of a chunk issued up front; the running
+  // maximum and weights are carried across chunks
   float M = kNegInf;
-  for (int i = 0; i < n_b; ++i) M = fmaxf(M, a.part_lse[row0 + (int64_t)i * a.H]);
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   float wsum = 0.f;
-  for (int i = 0; i < n_b; ++i) {
-    const int64_t row = row0 + (int64_t)i * a.H;
-    const float wgt = fast_exp2((a.part_lse[row] - M) * kLog2e);
-    const f32x4_t* po = (const f32x4_t*)(a.part_o + row * kVal) + 2 * lane;
-    wsum += wgt;
-    acc0 += wgt * po[0];
-    acc1 += wgt * po[1];
+  constexpr int kU = 8;
+  for (int c0 = 0; c0 < n_b; c0 += kU) {
+    float lv[kU];
+    f32x4_t o0[kU], o1[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int64_t row = row0 + (int64_t)(c0 + i) * a.H;
+      const bool ok = c0 + i < n_b;
+      const f32x4_t* po = (const f32x4_t*)(a.part_o + row * kVal) + 2 * lane;
+      lv[i] = ok ? a.part_lse[row] : kNegInf;
+      o0[i] = ok ? po[0] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      o1[i] = ok ? po[1] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) Mc = fmaxf(Mc, lv[i]);
+    if (c0 > 0) {
+      const float sc = fast_exp2((M - Mc) * kLog2e);
+      wsum *= sc;
+      acc0 *= sc;
+      acc1 *= sc;
+    }
+    M = Mc;
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const float wgt = c0 + i < n_b ? fast_exp2((lv[i] - M) * kLog2e) : 0.f;
+      wsum += wgt;
+      acc0 += wgt * o0[i];
+      acc1 += wgt * o1[i];
+    }
   }
   const float inv = 1.f / wsum;
   *dst = bf16x8_t{(__bf16)(acc0[0] * inv), (__bf16)(acc0[1] * inv), (__bf16)(acc0[2] * inv),

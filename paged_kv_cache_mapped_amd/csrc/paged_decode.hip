@@ -637,29 +637,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float M = kNegInf;
   f32x2_t acc = {0.f, 0.f};
   float wsum = 0.f;
+  // Chunks of kU partials, every load of a chunk issued up front; the
+  // running maximum and weights are carried across chunks (requests spanning
+  // more than kU pieces are common when lengths are short and many).
   constexpr int kU = 8;
-  if (n_b <= kU) {                  // common case: every load issued up front
+  for (int c0 = 0; c0 < n_b; c0 += kU) {
     float lv[kU];
     f32x2_t ov[kU];
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
-      lv[i] = i < n_b ? pl[i * a.Hq] : kNegInf;
-      ov[i] = i < n_b ? po[i * ostride] : f32x2_t{0.f, 0.f};
+      lv[i] = c0 + i < n_b ? pl[(c0 + i) * a.Hq] : kNegInf;
+      ov[i] = c0 + i < n_b ? po[(c0 + i) * ostride] : f32x2_t{0.f, 0.f};
     }
+    float Mc = M;
 #pragma unroll
-    for (int i = 0; i < kU; ++i) M = fmaxf(M, lv[i]);
+    for (int i = 0; i < kU; ++i) Mc = fmaxf(Mc, lv[i]);
+    if (c0 > 0) {
+      const float sc = fast_exp2((M - Mc) * kLog2e);
+      wsum *= sc;
+      acc *= sc;
+    }
+    M = Mc;
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
-      const float w = i < n_b ? fast_exp2((lv[i] - M) * kLog2e) : 0.f;
+      const float w = c0 + i < n_b ? fast_exp2((lv[i] - M) * kLog2e) : 0.f;
       wsum += w;
       acc += w * ov[i];
-    }
-  } else {
-    for (int i = 0; i < n_b; ++i) M = fmaxf(M, pl[i * a.Hq]);
-    for (int i = 0; i < n_b; ++i) {
-      const float w = fast_exp2((pl[i * a.Hq] - M) * kLog2e);
-      wsum += w;
-      acc += w * po[i * ostride];
     }
   }
   const float inv = 1.f / wsum;
