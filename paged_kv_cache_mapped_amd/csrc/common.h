@@ -7,6 +7,7 @@ namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -61,14 +62,15 @@ __device__ __forceinline__ bf16x8_t cat_tr(s16x4_t lo, s16x4_t hi) {
 }
 
 // Eight OCP e4m3fn codes -> eight bf16 values (exact: every e4m3fn value is a
-// bf16 value).  gfx950's v_cvt_pk_f32_fp8 decodes the OCP format.
+// bf16 value).  gfx950's v_cvt_scalef32_pk_bf16_fp8 decodes two OCP codes
+// (the low or the high half of the word) straight to bf16; a scale of 1
+// leaves the exponent as it is.
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(u32x2_t w) {
-  f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], false);
-  f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[0], true);
-  f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], false);
-  f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[1], true);
-  bf16x8_t r = {(__bf16)a[0], (__bf16)a[1], (__bf16)b[0], (__bf16)b[1],
-                (__bf16)c[0], (__bf16)c[1], (__bf16)d[0], (__bf16)d[1]};
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  const bf16x8_t r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   return r;
 }
 

@@ -1123,7 +1123,6 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(AttnArgs a) {
     acc += w * *((const f32x2_t*)(a.part_o + (p * stride + rh) * kD) + lane);
   }
   const float inv = 1.f / wsum;
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   *(bf16x2_t*)(a.out + rh * kD + 2 * lane) = bf16x2_t{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
   if (lane == 0 && a.lse) a.lse[rh] = M + __log2f(wsum) * kLn2;
 }

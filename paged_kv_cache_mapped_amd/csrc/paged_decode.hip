@@ -613,7 +613,6 @@ void decode_piece_kernel(DecodeArgs a) {
 // than one piece.  One wave per (request, query head).  A request of length 0
 // has no visible key: its output is 0 and its lse -inf.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int64_t bh = (int64_t)blockIdx.x * 4 + wave;
   if (bh >= (int64_t)a.batch * a.Hq) return;

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import paged_kv_cache_mapped_amd as pk
-from oracle import attention as oa, bf16 as ob, cache as oc
+from oracle import attention as oa, bf16 as ob, cache as oc, fp8 as of8
 from synth import workloads as w
 
 from .gpu_util import (BF16_TOL, FP8_TOL, LSE_TOL, bf16_to_f64, dev, device_cache, max_err,
@@ -208,3 +208,34 @@ def test_decode_empty_requests(split):
     ro, rl = oa.paged_decode(ob.to_f64(st.q[empty]), oracle_cache(st.cache),
                              st.block_tables[empty], lens[empty], st.scale)
     assert (ro == 0).all() and np.isneginf(rl).all()        # the oracle's reading agrees
+
+
+@pytest.mark.parametrize("layout", ["nhd", "preshuffled"])
+def test_decode_fp8_every_code(layout):
+    """Every e4m3fn code through the decode's fp8 read: two requests of one
+    token each, whose V rows carry codes 0..127 and 128..255 (the two NaN
+    codes replaced by 0).  With one key the softmax weight is exactly 1, so
+    with unit scales the output is each code's value, bit for bit (every
+    e4m3fn value is a bf16 value).  The cache is placed by the oracle's
+    write of those values, which round-trips them to the same codes."""
+    st = w.decode_workload(16, 2, 4, 2, 128, 16, 64, 1, 1, layout=layout, dtype="fp8",
+                           fixed_lens=[1, 1])
+    codes = np.arange(256).astype(np.uint8).reshape(2, 128)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    vals = of8.decode(codes)
+    vbits = w.f32_to_bf16_bits(vals.astype(np.float32))
+    v_new = np.ascontiguousarray(np.broadcast_to(vbits[:, None, :], (2, 2, 128)))
+    sp = st.cache.spec
+    base = oc.Cache(st.cache.k, st.cache.v, sp.layout, sp.dtype, sp.block_size, sp.num_kv_heads,
+                    sp.head_dim, sp.x, 1.0, 1.0)
+    ocache = oc.write(base, st.k_new, v_new, st.slot_mapping)
+    dc = pk.PagedKVCache(dev(ocache.k), dev(ocache.v), sp.block_size, sp.num_kv_heads,
+                         sp.head_dim, sp.layout, sp.dtype, 1.0, 1.0)
+    say(f"decode fp8 every code {layout}")
+    out, lse = _run(dc, st)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, h], vals[b]), (b, h)
+    ro, rl = oa.paged_decode(ob.to_f64(st.q), ocache, st.block_tables, st.seq_lens, st.scale)
+    assert np.array_equal(ro, np.broadcast_to(vals[:, None, :], ro.shape))   # the oracle agrees
+    assert max_err(lse, rl) <= LSE_TOL
