@@ -41,6 +41,11 @@ over one batch of seeded synthetic input that is already resident in HBM:
 The default run measures the headline and then every other workload as a
 "secondary" entry, each with its roofline and its CPU-oracle baseline.
 
+Before the W warm-up steps of each workload, the step runs untimed for
+SETTLE_S of wall time ("settle": steps and ms in the line): coming out of idle
+the GPU needs some tens of milliseconds of sustained work to reach its steady
+clocks, and W steps of a sub-millisecond step would time the ramp instead.
+
 Per call, after the timed region: the average device time from HIP events
 around the call alone ("ms"), and for decode calls also with the L2 and MALL
 flushed before each call by a 512 MB read outside the event pair ("ms_cold",
@@ -72,6 +77,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+SETTLE_S = 0.25                # untimed sustained work before each workload's warm-up
+SETTLE_MAX_STEPS = 2000
 
 METRIC = "paged decode HBM GB/s (% of 8 TB/s); mixed-batch attention tokens/s"
 
@@ -743,10 +750,24 @@ def main():
             for c in calls:
                 c.fn()
 
+        # Clock settle: the GPU comes to each workload out of idle (the batch
+        # was just built on the host) at reduced clocks, and its step time
+        # keeps falling over the first tens of milliseconds of sustained work
+        # (3-13 % on these workloads).  The step is repeated, untimed, for
+        # SETTLE_S of wall time (at most SETTLE_MAX_STEPS), then the W
+        # warm-up steps run as asked.
+        settle_steps, t_settle = 0, time.perf_counter()
+        while (time.perf_counter() - t_settle < SETTLE_S and settle_steps < SETTLE_MAX_STEPS):
+            for _ in range(4):
+                step()
+            settle_steps += 4
+            torch.cuda.synchronize()
+        settle_ms = (time.perf_counter() - t_settle) * 1e3
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        _log(f"timing {args.steps} steps of {name}")
+        _log(f"timing {args.steps} steps of {name} (after {settle_steps} settle steps, "
+             f"{settle_ms:.0f} ms)")
         # HIP events on the stream the library launches on, around the dominant
         # call of every timed step (events between every pair of calls would add
         # a marker packet each to the step)
@@ -839,7 +860,8 @@ def main():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         return {"value": value, "unit": unit, "ms": ms, "device_ms": device_ms, "config": config,
-                "roofline": roof, "calls": per, "cpu": cpu}
+                "roofline": roof, "calls": per, "cpu": cpu,
+                "settle": {"steps": settle_steps, "ms": round(settle_ms, 1)}}
 
     with_cpu = not args.no_cpu_baseline
     main_r = measure(args.workload, with_cpu)
@@ -849,7 +871,8 @@ def main():
             r = measure(name, with_cpu)
             e = {"metric": SECONDARY_METRIC[name], "value": round(r["value"], 1),
                  "unit": r["unit"], "ms_per_step": round(r["ms"], 4),
-                 "device_ms_per_step": round(r["device_ms"], 4), "config": r["config"],
+                 "device_ms_per_step": round(r["device_ms"], 4), "settle": r["settle"],
+                 "config": r["config"],
                  "roofline": r["roofline"], "cpu_baseline": r["cpu"], "calls": r["calls"]}
             if name == "heavy_tailed_mixed_batch":
                 c = r["calls"]
@@ -867,7 +890,8 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "settle": main_r["settle"],
+        "ms_per_step": round(ms, 4),
         "device_ms_per_step": round(main_r["device_ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded numpy PCG64; no datasets or weights)",
