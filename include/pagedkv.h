@@ -227,7 +227,8 @@ int prefill_attn(const void* q, const void* k, const void* v,
  *   out           [total_new][num_q_heads][head_dim] bf16
  *   lse           [total_new][num_q_heads] fp32 or NULL
  *   scale         softmax scale, finite and > 0 (else KV_EINVAL)
- *   workspace     >= extend_attn_workspace_bytes(...) bytes (0 in fused mode)
+ *   workspace     >= extend_attn_workspace_bytes(...) bytes (0 in fused mode;
+ *                 in automatic mode a smaller one forgoes the work list)
  * New token i of a request with C cached tokens sits at position C + i and
  * sees cached tokens 0..C-1 and new tokens 0..i.  Caches: NHD (any block
  * size) or preshuffled (block size 16), bf16 or fp8; the context is read in
@@ -246,7 +247,14 @@ int prefill_attn(const void* q, const void* k, const void* v,
  *         same order) and then the new tokens with one running softmax
  *         state: the merge happens in registers and no workspace is used.
  * extend_attn picks fused when the new tokens alone fill the GPU (or there is
- * no context), else split; extend_attn_ex lets the caller choose.
+ * no context), else split; extend_attn_ex lets the caller choose.  A fused
+ * pick whose longest context spans two or more chunks (at most 1024
+ * requests) runs from a work list built on the GPU: every query item of the
+ * batch, requests heaviest first, with the requests whose fused walk would
+ * hold workgroups beyond half the batch's mean load per CU run split (their
+ * chunks in parallel; at most 16 such requests and 64 MiB of fp32 partials)
+ * and merged as above.  extend_attn_workspace_bytes then counts the plan, the
+ * list and those partials; a smaller workspace runs plain fused.
  * ------------------------------------------------------------------------- */
 size_t extend_attn_workspace_bytes(const kv_cache_t* cache, int32_t num_seqs,
                                    int32_t total_new_tokens, int32_t num_q_heads,

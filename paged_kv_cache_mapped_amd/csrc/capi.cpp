@@ -265,7 +265,7 @@ size_t extend_attn_workspace_bytes_ex(const kv_cache_t* cache, int32_t num_seqs,
     return 0;
   const pkv::ExtendPlan p =
       pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len, budget, mode, nullptr);
-  return pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
+  return pkv::extend_workspace_bytes(p, num_seqs, total_new, num_q_heads, cache->head_dim);
 }
 
 size_t extend_attn_workspace_bytes(const kv_cache_t* cache, int32_t num_seqs, int32_t total_new,
@@ -298,9 +298,13 @@ int extend_attn_ex(const kv_cache_t* cache, const void* q, const void* k_new, co
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
     return fail(KV_EINVAL, "%s: q, k_new, v_new and out must be 16-byte aligned", fn);
   if (num_q_heads > 65535 || num_seqs > 65535) return fail(KV_EINVAL, "%s: grid too large", fn);
-  const pkv::ExtendPlan p = pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len,
-                                             budget, mode, (hipStream_t)stream);
-  const size_t need = pkv::extend_workspace_bytes(p, total_new, num_q_heads, cache->head_dim);
+  pkv::ExtendPlan p = pkv::plan_extend(*cache, num_seqs, total_new, num_q_heads, max_ctx_len,
+                                       budget, mode, (hipStream_t)stream);
+  size_t need = pkv::extend_workspace_bytes(p, num_seqs, total_new, num_q_heads, cache->head_dim);
+  if (p.hybrid && (!workspace || workspace_bytes < need || !aligned16(workspace))) {
+    p.hybrid = 0;                 // no room for the hybrid plan: plain fused
+    need = 0;
+  }
   if (need > 0) {
     if (!workspace) return fail(KV_EINVAL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
     if (workspace_bytes < need)

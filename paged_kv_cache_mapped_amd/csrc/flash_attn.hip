@@ -91,6 +91,13 @@ struct AttnArgs {
   float ctx_qk_mult;        // scale * k_scale * log2(e)
   float ctx_vexp;           // log2(v_scale): added to the exponent of p
   float ctx_linv;           // 1 / v_scale: takes it back out of the row sum
+  // hybrid extend (see extend_plan_kernel): the plan and the work list in
+  // the workspace
+  const int32_t* plan;
+  const struct ListEntry* list;
+  int32_t max_split;        // split request slots
+  int32_t list_cap;         // work-list entries the workspace holds
+  int32_t plan_slots;       // workgroups the GPU holds at once (one per CU)
 };
 
 // Work order.  A work item is (lane, query item), lanes being the
@@ -118,22 +125,27 @@ struct WorkItem {
   int32_t qi;
 };
 template <class Args>
-__device__ __forceinline__ WorkItem work_item(const Args& a, int64_t L) {
-  const int64_t hx = a.grid_pad / (8 * (int64_t)a.n_qitems);
+__device__ __forceinline__ WorkItem work_item_in(const Args& a, int64_t L, int64_t grid_pad,
+                                                 int32_t n_qitems) {
+  const int64_t hx = grid_pad / (8 * (int64_t)n_qitems);
   const int64_t j = L >> 3;
   WorkItem w;
   int64_t l;                    // this XCD's l-th lane
   if (a.qt_major) {
-    w.qi = a.n_qitems - 1 - (int32_t)(j / hx);
+    w.qi = n_qitems - 1 - (int32_t)(j / hx);
     l = j % hx;
   } else {
-    w.qi = a.n_qitems - 1 - (int32_t)(j % a.n_qitems);
-    l = j / a.n_qitems;
+    w.qi = n_qitems - 1 - (int32_t)(j % n_qitems);
+    l = j / n_qitems;
   }
   // chunks of lchunk consecutive lanes are dealt to the XCDs in turn
   const int64_t c = a.lchunk;
   w.lane = ((l / c) * 8 + (L & 7)) * c + l % c;
   return w;
+}
+template <class Args>
+__device__ __forceinline__ WorkItem work_item(const Args& a, int64_t L) {
+  return work_item_in(a, L, a.grid_pad, a.n_qitems);
 }
 static int64_t work_grid(int64_t lanes, int32_t n_qitems, int32_t lchunk) {
   return 8 * (((lanes + 8 * lchunk - 1) / (8 * lchunk)) * lchunk) * (int64_t)n_qitems;
@@ -989,23 +1001,29 @@ void prefill_stream_kernel(AttnArgs) {
 // tokens among themselves (causal).  Part
 // p >= 1: the new tokens against context chunk p-1 = cached tokens
 // [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
-// fp32 partial; extend_merge_kernel combines them.
+// fp32 partial (row pbase + i for new token i); extend_merge_kernel combines
+// them.
+// Hybrid plan, in the workspace (int32): [0] requests run split, [1] compact
+// partial rows they use, [2] work-list entries, [3] unused, then max_split
+// request ids and max_split first compact rows; after it (256-byte aligned)
+// the work list, one ListEntry per (request, query item) of a fused request
+// and per (request, part, query item) of a split one, heaviest first.
+constexpr int kPlanHead = 4;
+constexpr int kHybridMaxSeqs = 1024;          // requests the plan takes
+constexpr int kHybridMaxSplit = 16;           // requests that may run split
+constexpr int64_t kHybridPartialBytes = 64ll << 20;
+constexpr int kListSortMax = 2048;            // longer lists keep request order
+struct ListEntry {
+  int32_t seq, slot, part, qi;                // slot -1: fused
+};
+
 template <int KIND>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
-void extend_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
-  const WorkItem w = work_item(a, blockIdx.x);
-  if (w.lane >= a.items) return;
-  int64_t rest = w.lane;
-  const int32_t gsel = (int32_t)(rest % a.Gs);
-  rest /= a.Gs;
-  const int32_t hkv = (int32_t)(rest % a.Hkv);
-  rest /= a.Hkv;
-  const int32_t part = (int32_t)(rest % a.n_parts);
-  const int32_t seq = (int32_t)(rest / a.n_parts);
+__device__ __forceinline__ void split_item(const AttnArgs& a, uint8_t* smem, int32_t seq,
+                                           int32_t part, int32_t hkv, int32_t gsel, int32_t qi,
+                                           int32_t slot) {
   const int32_t s0 = a.cu[seq];
   const int32_t qn = a.cu[seq + 1] - s0;
-  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+  const RowBlock rb = row_block(a, hkv, gsel, qi);
   if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   RowState S;
   if (part == 0) {
@@ -1020,7 +1038,25 @@ void extend_kernel(AttnArgs a) {
     run_keys<true, false, true, KIND>(a, smem, paged_keys(a, seq, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
                                       qn, kb, min(C, kb + a.chunk_tokens), S);
   }
-  finish_rows<true>(a, rb.h, s0, rb.q0, qn, part, S);
+  // partial rows: the request's own rows, or (hybrid, slot >= 0) its compact rows
+  const int64_t pbase = slot < 0 ? s0 : uniform(a.plan[kPlanHead + a.max_split + slot]);
+  finish_rows<true>(a, rb.h, pbase, rb.q0, qn, part, S);
+}
+
+template <int KIND>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void extend_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  const WorkItem w = work_item(a, blockIdx.x);
+  if (w.lane >= a.items) return;
+  int64_t rest = w.lane;
+  const int32_t gsel = (int32_t)(rest % a.Gs);
+  rest /= a.Gs;
+  const int32_t hkv = (int32_t)(rest % a.Hkv);
+  rest /= a.Hkv;
+  const int32_t part = (int32_t)(rest % a.n_parts);
+  const int32_t seq = (int32_t)(rest / a.n_parts);
+  split_item<KIND>(a, smem, seq, part, hkv, gsel, w.qi, -1);
 }
 
 // Fused extend, used when the batch has enough query tiles to fill the GPU
@@ -1036,19 +1072,11 @@ void extend_kernel(AttnArgs a) {
 // per-wave LDS regions and the output leaves through them, as in the
 // persistent prefill.
 template <int KIND>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
-void extend_fused_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kQArea + kWaves * kQRegion];
-  const WorkItem w = work_item(a, blockIdx.x);
-  if (w.lane >= a.items) return;
-  int64_t rest = w.lane;
-  const int32_t gsel = (int32_t)(rest % a.Gs);
-  rest /= a.Gs;
-  const int32_t hkv = (int32_t)(rest % a.Hkv);
-  const int32_t seq = (int32_t)(rest / a.Hkv);
+__device__ __forceinline__ void fused_item(const AttnArgs& a, uint8_t* smem, int32_t seq,
+                                           int32_t hkv, int32_t gsel, int32_t qi) {
   const int32_t s0 = a.cu[seq];
   const int32_t qn = a.cu[seq + 1] - s0;
-  const RowBlock rb = row_block(a, hkv, gsel, w.qi);
+  const RowBlock rb = row_block(a, hkv, gsel, qi);
   if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   const int32_t C = context_len(a, seq);
   StreamItem it = {};
@@ -1091,6 +1119,42 @@ void extend_fused_kernel(AttnArgs a) {
   store_rows(a, smem, rb.h, s0, it.q0w, qn, S);
 }
 
+template <int KIND>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void extend_fused_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQArea + kWaves * kQRegion];
+  const WorkItem w = work_item(a, blockIdx.x);
+  if (w.lane >= a.items) return;
+  int64_t rest = w.lane;
+  const int32_t gsel = (int32_t)(rest % a.Gs);
+  rest /= a.Gs;
+  const int32_t hkv = (int32_t)(rest % a.Hkv);
+  const int32_t seq = (int32_t)(rest / a.Hkv);
+  fused_item<KIND>(a, smem, seq, hkv, gsel, w.qi);
+}
+
+// Hybrid extend over the plan's work list: lanes are the (KV head, pair or
+// head) combinations, query items the list positions (heaviest first, the
+// positions past the list's length empty and launched last).  An entry runs
+// fused (its request's context and new tokens, one running state) or as one
+// part of a split request (partials in compact rows, merged afterwards).
+template <int KIND>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void extend_list_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQArea + kWaves * kQRegion];
+  const WorkItem w = work_item(a, blockIdx.x);
+  if (w.lane >= a.items) return;
+  const int32_t pos = a.n_qitems - 1 - w.qi;
+  if (pos >= uniform(a.plan[2])) return;
+  const ListEntry* e = a.list + pos;
+  const int32_t seq = uniform(e->seq), slot = uniform(e->slot);
+  const int32_t part = uniform(e->part), qi = uniform(e->qi);
+  const int32_t gsel = (int32_t)(w.lane % a.Gs);
+  const int32_t hkv = (int32_t)(w.lane / a.Gs);
+  if (slot < 0) fused_item<KIND>(a, smem, seq, hkv, gsel, qi);
+  else split_item<KIND>(a, smem, seq, part, hkv, gsel, qi, slot);
+}
+
 // Final merge of the extend parts of each (row, head), one wave each:
 // o = sum_p w_p o_p / sum_p w_p, w_p = exp(lse_p - max_p lse_p),
 // lse = max + ln sum_p w_p.
@@ -1125,6 +1189,187 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(AttnArgs a) {
   const float inv = 1.f / wsum;
   *(bf16x2_t*)(a.out + rh * kD + 2 * lane) = bf16x2_t{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
   if (lane == 0 && a.lse) a.lse[rh] = M + __log2f(wsum) * kLn2;
+}
+
+// Plan of the hybrid extend (one workgroup).  A fused work item of request b
+// (n_b new tokens, C_b cached) with rows [i R, (i+1) R) walks ceil(C_b/64)
+// context tiles and ceil(min((i+1) R, n_b)/64) new-token tiles (R = 128 rows
+// for head pairs, 256 for two row tiles of one head); its longest item walks
+// walk_b = ceil(C_b/64) + ceil(n_b/64).  The batch's work, summed over every
+// item, spread over the resident workgroups gives the mean load D.  A request
+// with walk_b > D / 2 holds workgroups for a large part of the kernel's time
+// by itself, and late if they start late; if its context spans more than one
+// chunk it runs split (its chunks in parallel), while slots (max_split) and
+// compact partial rows (rows: the workspace holds n_parts x rows partials)
+// last, in request order.  Then the work list: every query item of a fused
+// request and every (part, query item) of a split one, with its walk as its
+// cost, sorted by request (heaviest request first) and within a request
+// heaviest first, when it has at most kListSortMax entries.
+__global__ __launch_bounds__(1024) void extend_plan_kernel(AttnArgs a) {
+  __shared__ int32_t s_c[kHybridMaxSeqs], s_n[kHybridMaxSeqs], s_slot[kHybridMaxSeqs];
+  __shared__ int32_t s_off[kHybridMaxSeqs + 1];
+  __shared__ int64_t s_w[16];
+  __shared__ int32_t s_wsum[16];
+  __shared__ uint64_t s_key[kListSortMax];
+  __shared__ ListEntry s_ent[kListSortMax];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t R = a.pairs ? kBM : 2 * kBM;
+  int32_t* plan = (int32_t*)a.plan;
+  int64_t w = 0;
+  for (int32_t b = t; b < a.num_seqs; b += 1024) {
+    const int32_t n = a.cu[b + 1] - a.cu[b];
+    const int32_t C = context_len(a, b);
+    s_c[b] = C;
+    s_n[b] = n;
+    s_slot[b] = -1;
+    if (n > 0) {
+      const int64_t k = (n + R - 1) / R;                  // query items per lane
+      const int64_t ct = (C + kBN - 1) / kBN;
+      w += (int64_t)a.Hkv * a.Gs * (k * ct + (R / kBN) * (k - 1) * k / 2 + (n + kBN - 1) / kBN);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
+  if (lane == 0) s_w[wave] = w;
+  __syncthreads();
+  if (t == 0) {
+    int64_t tot = 0;
+    for (int i = 0; i < 16; ++i) tot += s_w[i];
+    const int64_t D = tot / (a.plan_slots > 0 ? a.plan_slots : 1);
+    int32_t n_split = 0, used = 0;
+    for (int32_t b = 0; b < a.num_seqs && n_split < a.max_split; ++b) {
+      const int32_t C = s_c[b], n = s_n[b];
+      const int64_t walk = (C + kBN - 1) / kBN + (n + kBN - 1) / kBN;
+      if (n > 0 && 2 * walk > D && C > a.chunk_tokens && used + n <= a.rows) {
+        plan[kPlanHead + n_split] = b;
+        plan[kPlanHead + a.max_split + n_split] = used;
+        s_slot[b] = n_split;
+        used += n;
+        ++n_split;
+      }
+    }
+    plan[0] = n_split;
+    plan[1] = used;
+  }
+  __syncthreads();
+  // entries per request (one request per thread) and their exclusive offsets
+  int32_t cnt = 0;
+  if (t < a.num_seqs && s_n[t] > 0) {
+    const int32_t k = (s_n[t] + R - 1) / R;
+    int32_t np = 1 + (s_c[t] + a.chunk_tokens - 1) / a.chunk_tokens;
+    np = np > a.n_parts ? a.n_parts : np;
+    cnt = s_slot[t] < 0 ? k : np * k;
+  }
+  int32_t inc = cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
+  }
+  if (lane == 63) s_wsum[wave] = inc;
+  __syncthreads();
+  int32_t base = 0;
+  for (int i = 0; i < wave; ++i) base += s_wsum[i];
+  if (t < a.num_seqs) s_off[t] = base + inc - cnt;
+  if (t == 1023) s_off[a.num_seqs] = base + inc;
+  __syncthreads();
+  const int32_t total = s_off[a.num_seqs];
+  const int32_t E = total < a.list_cap ? total : a.list_cap;
+  const bool sorted = E <= kListSortMax;
+  ListEntry* list = (ListEntry*)a.list;
+  if (cnt > 0) {
+    const int32_t n = s_n[t], C = s_c[t], slot = s_slot[t];
+    const int32_t k = (n + R - 1) / R;
+    const int32_t ct = (C + kBN - 1) / kBN;
+    // the request's heaviest entry: its last query item (fused), else its
+    // last query item of the new tokens or a whole chunk (split)
+    const int32_t nt = (n + kBN - 1) / kBN;
+    const int32_t cht = ((C < a.chunk_tokens ? C : a.chunk_tokens) + kBN - 1) / kBN;
+    const int32_t rcost = slot < 0 ? ct + nt : (nt > cht ? nt : cht);
+    const uint64_t rkey = ((uint64_t)(0xFFFFu - (uint32_t)(rcost < 0xFFFF ? rcost : 0xFFFF)) << 48) |
+                          ((uint64_t)t << 32);
+    for (int32_t i = 0; i < cnt; ++i) {
+      const int32_t idx = s_off[t] + i;
+      if (idx >= E) break;
+      ListEntry e;
+      int32_t cost;
+      e.seq = t;
+      e.slot = slot;
+      e.qi = i % k;
+      e.part = slot < 0 ? 0 : i / k;
+      const int32_t rows_to = min((e.qi + 1) * R, n);
+      if (slot < 0) {
+        cost = ct + (rows_to + kBN - 1) / kBN;
+      } else if (e.part == 0) {
+        cost = (rows_to + kBN - 1) / kBN;
+      } else {
+        const int32_t left = C - (e.part - 1) * a.chunk_tokens;
+        cost = ((left < a.chunk_tokens ? left : a.chunk_tokens) + kBN - 1) / kBN;
+      }
+      if (sorted) {
+        // requests heaviest first, each request's entries heaviest first:
+        // the lanes of a request run together and share its K/V in L2
+        s_ent[idx] = e;
+        const uint64_t c16 = (uint64_t)(cost < 0xFFFF ? cost : 0xFFFF);
+        s_key[idx] = rkey | ((0xFFFFull - c16) << 11) | (uint64_t)idx;
+      } else {
+        list[idx] = e;
+      }
+    }
+  }
+  if (sorted) {
+    int32_t N = 2;
+    while (N < E) N <<= 1;
+    for (int32_t i = E + t; i < N; i += 1024) s_key[i] = ~0ull;
+    __syncthreads();
+    for (int32_t kk = 2; kk <= N; kk <<= 1) {
+      for (int32_t jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int32_t i = t; i < N; i += 1024) {
+          const int32_t ixj = i ^ jj;
+          if (ixj > i) {
+            const uint64_t x = s_key[i], y = s_key[ixj];
+            if ((x > y) == ((i & kk) == 0)) {
+              s_key[i] = y;
+              s_key[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int32_t i = t; i < E; i += 1024) list[i] = s_ent[s_key[i] & 0x7FFull];
+  }
+  if (t == 0) plan[2] = E;
+}
+
+// Merge of the hybrid extend's split requests: one wave per compact (row,
+// head), as extend_merge_kernel.
+__global__ __launch_bounds__(256) void extend_merge_compact_kernel(AttnArgs a) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + wave;
+  const int32_t n_split = uniform(a.plan[0]), used = uniform(a.plan[1]);
+  if (rh >= (int64_t)used * a.Hq) return;
+  const int32_t cr = (int32_t)(rh / a.Hq), h = (int32_t)(rh % a.Hq);
+  int32_t j = 0;                                          // the slot owning compact row cr
+  while (j + 1 < n_split && a.plan[kPlanHead + a.max_split + j + 1] <= cr) ++j;
+  const int32_t seq = a.plan[kPlanHead + j];
+  const int64_t grow = (int64_t)a.cu[seq] + (cr - a.plan[kPlanHead + a.max_split + j]);
+  const int32_t C = context_len(a, seq);
+  int32_t np = 1 + (C + a.chunk_tokens - 1) / a.chunk_tokens;
+  np = np > a.n_parts ? a.n_parts : np;
+  const int64_t stride = (int64_t)a.rows * a.Hq;
+  float M = kNegInf;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_lse[p * stride + rh]);
+  f32x2_t acc = {0.f, 0.f};
+  float wsum = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float lp = a.part_lse[p * stride + rh];
+    const float wp = lp == kNegInf ? 0.f : fast_exp2((lp - M) * kLog2e);
+    wsum += wp;
+    acc += wp * *((const f32x2_t*)(a.part_o + (p * stride + rh) * kD) + lane);
+  }
+  const float inv = 1.f / wsum;
+  const int64_t oh = grow * a.Hq + h;
+  *(bf16x2_t*)(a.out + oh * kD + 2 * lane) = bf16x2_t{(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
+  if (lane == 0 && a.lse) a.lse[oh] = M + __log2f(wsum) * kLn2;
 }
 
 int32_t log2i(int32_t v) {
@@ -1199,16 +1444,44 @@ ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
     p.fused = 1;
   else
     p.fused = (p.n_chunks == 0 || tiles >= (int64_t)4 * device_cu_count(stream)) ? 1 : 0;
+  // Automatic and fused with a context of two or more chunks: hybrid, whose
+  // device-side plan may still run some requests split (their partials in at
+  // most kHybridPartialBytes of compact rows).
+  p.hybrid = 0;
+  p.max_split = 0;
+  p.cap_rows = 0;
+  p.list_cap = 0;
+  if (mode == KV_EXTEND_AUTO && p.fused && p.n_chunks >= 2 && num_seqs <= kHybridMaxSeqs) {
+    const int64_t per_row = (int64_t)p.n_parts * num_q_heads * (kD + 1) * (int64_t)sizeof(float);
+    const int64_t cap = kHybridPartialBytes / per_row;
+    p.cap_rows = (int32_t)(cap < total_new ? cap : total_new);
+    p.max_split = num_seqs < kHybridMaxSplit ? num_seqs : kHybridMaxSplit;
+    // list length bound: a fused request has at most n/R + 1 query items, a
+    // split one n_parts times that, and the split requests' rows are at most
+    // cap_rows
+    const int64_t R = (num_q_heads / c.num_kv_heads) % 2 == 0 ? kBM : 2 * kBM;
+    const int64_t cap_list = (total_new + R - 1) / R + num_seqs +
+                             (int64_t)p.n_parts * ((p.cap_rows + R - 1) / R + p.max_split);
+    p.list_cap = (int32_t)(cap_list < (1 << 24) ? cap_list : 0);
+    p.hybrid = p.cap_rows > 0 && p.list_cap > 0 && p.n_parts < (1 << 15) ? 1 : 0;
+  }
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
-                              int32_t head_dim) {
-  if (p.fused) return 0;
-  const size_t rows = (size_t)p.n_parts * total_new * num_q_heads;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+static size_t hybrid_plan_bytes(const ExtendPlan& p) {
+  return align256(sizeof(int32_t) * ((size_t)kPlanHead + 2 * (size_t)p.max_split)) +
+         align256(sizeof(ListEntry) * (size_t)p.list_cap);
+}
+
+size_t extend_workspace_bytes(const ExtendPlan& p, int32_t num_seqs, int32_t total_new,
+                              int32_t num_q_heads, int32_t head_dim) {
+  if (p.fused && !p.hybrid) return 0;
+  const int32_t rows_cap = p.fused ? p.cap_rows : total_new;
+  const size_t rows = (size_t)p.n_parts * rows_cap * num_q_heads;
+  return (p.fused ? hybrid_plan_bytes(p) : 0) + align256(rows * head_dim * sizeof(float)) +
+         align256(rows * sizeof(float));
 }
 
 hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,
@@ -1228,9 +1501,13 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.ctx_lens = ctx_lens;
   a.out = (__bf16*)out;
   a.lse = lse;
-  const size_t prow = (size_t)p.n_parts * total_new * num_q_heads;
-  a.part_o = (float*)workspace;
-  a.part_lse = (float*)((uint8_t*)workspace + align256(prow * c.head_dim * sizeof(float)));
+  const size_t plan_bytes = p.fused && p.hybrid ? hybrid_plan_bytes(p) : 0;
+  const size_t prow = (size_t)p.n_parts * (p.fused ? p.cap_rows : total_new) * num_q_heads;
+  a.plan = (const int32_t*)workspace;
+  a.list = (const ListEntry*)((uint8_t*)workspace +
+                              align256(sizeof(int32_t) * ((size_t)kPlanHead + 2 * (size_t)p.max_split)));
+  a.part_o = (float*)((uint8_t*)workspace + plan_bytes);
+  a.part_lse = (float*)((uint8_t*)workspace + plan_bytes + align256(prow * c.head_dim * sizeof(float)));
   a.max_blocks = max_blocks > 0 ? max_blocks : 1;
   a.num_blocks = c.num_blocks;
   a.bs = c.block_size;
@@ -1251,6 +1528,37 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.qt_major = n_qtiles <= 16 ? 1 : 0;
   const int kind = c.layout == KV_LAYOUT_NHD ? (c.dtype == KV_DTYPE_BF16 ? kCtxNhdBf16 : kCtxNhdFp8)
                                              : (c.dtype == KV_DTYPE_BF16 ? kCtxPreBf16 : kCtxPreFp8);
+  if (p.fused && p.hybrid) {
+    a.rows = p.cap_rows;
+    a.max_split = p.max_split;
+    a.list_cap = p.list_cap;
+    a.plan_slots = device_cu_count(s);
+    a.items = (int64_t)a.Hkv * a.Gs;                     // lanes: (KV head, pair or head)
+    a.n_qitems = p.list_cap;                             // list positions
+    a.qt_major = 1;
+    // an XCD's share of the lanes: an eighth of them, within one KV head or
+    // whole KV heads, so that its workgroups stream one context at a time
+    {
+      const int32_t target = a.items >= 8 ? (int32_t)(a.items / 8) : 1;
+      int32_t c = 1;
+      if (target >= a.Gs) c = (target / a.Gs) * a.Gs;
+      else for (int32_t d = target; d >= 1; --d) if (a.Gs % d == 0) { c = d; break; }
+      a.lchunk = c;
+    }
+    a.grid_pad = work_grid(a.items, a.n_qitems, a.lchunk);
+    if (a.grid_pad > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(extend_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+    const dim3 grid((unsigned)a.grid_pad);
+    switch (kind) {
+      case kCtxNhdBf16: hipLaunchKernelGGL(extend_list_kernel<kCtxNhdBf16>, grid, dim3(kThreads), 0, s, a); break;
+      case kCtxNhdFp8: hipLaunchKernelGGL(extend_list_kernel<kCtxNhdFp8>, grid, dim3(kThreads), 0, s, a); break;
+      case kCtxPreBf16: hipLaunchKernelGGL(extend_list_kernel<kCtxPreBf16>, grid, dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL(extend_list_kernel<kCtxPreFp8>, grid, dim3(kThreads), 0, s, a); break;
+    }
+    const int64_t rh = (int64_t)p.cap_rows * num_q_heads;
+    hipLaunchKernelGGL(extend_merge_compact_kernel, dim3((unsigned)((rh + 3) / 4)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (p.fused) {
     a.items = (int64_t)num_seqs * a.Hkv * a.Gs;          // lanes
     a.grid_pad = work_grid(a.items, a.n_qitems, a.lchunk);

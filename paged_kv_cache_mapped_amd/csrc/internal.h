@@ -87,12 +87,19 @@ struct ExtendPlan {
   int32_t n_chunks;       // context chunks of the longest context
   int32_t n_parts;        // n_chunks + 1 (the new-token part)
   int32_t fused;          // 1: one workgroup runs every part of its rows (no partials)
+  // hybrid (automatic mode, fused plan, context over two or more chunks): a
+  // device-side plan runs the requests whose walk would outlast the rest
+  // split, in compact partial rows; 0 when the workspace is too small for it
+  int32_t hybrid;
+  int32_t max_split;      // requests that may run split
+  int32_t cap_rows;       // compact partial rows
+  int32_t list_cap;       // work-list entries
 };
 ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
                        int32_t num_q_heads, int32_t max_ctx_len, int32_t chunk_budget_tokens,
                        int32_t mode, hipStream_t stream);
-size_t extend_workspace_bytes(const ExtendPlan& p, int32_t total_new, int32_t num_q_heads,
-                              int32_t head_dim);
+size_t extend_workspace_bytes(const ExtendPlan& p, int32_t num_seqs, int32_t total_new,
+                              int32_t num_q_heads, int32_t head_dim);
 hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q,
                          const void* k_new, const void* v_new, const int32_t* cu_q_lens,
                          const int32_t* ctx_lens, const int32_t* tables, int32_t max_blocks,

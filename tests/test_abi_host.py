@@ -203,7 +203,8 @@ def test_attention_calls_reject_bad_scales(scale):
 
 def test_extend_workspace_by_mode():
     """Fused extend needs no workspace; split extend needs one fp32 (o, lse)
-    partial per (part, row, query head): parts = context chunks + 1."""
+    partial per (part, row, query head): parts = context chunks + 1; the
+    automatic (hybrid) one a plan and a bounded block of compact partials."""
     L = pk.lib()
     c = _cache(num_kv_heads=8, num_blocks=16384)
     a256 = lambda x: -(-x // 256) * 256
@@ -214,7 +215,21 @@ def test_extend_workspace_by_mode():
     parts = -(-mctx // chunk) + 1                     # 7 chunks + the new tokens
     rows = parts * T * Hq
     assert ws(pk.KV_EXTEND_SPLIT) == a256(rows * 128 * 4) + a256(rows * 4)
-    assert ws(pk.KV_EXTEND_AUTO) in (0, ws(pk.KV_EXTEND_SPLIT))
+    # automatic: 128 query tiles x 64 heads fill 256 CUs -> fused, and a
+    # context of 7 chunks -> hybrid: the plan (4 header words, per split slot
+    # a request and a first compact row), the work list (16 bytes per entry:
+    # at most T/R + E query items of fused requests and n_parts x (cap_rows/R
+    # + slots) of split ones, R = 128 rows for head pairs) and the partials of
+    # at most 64 MiB of compact rows
+    slots = min(E, 16)
+    cap_rows = min(T, (64 << 20) // (parts * Hq * 129 * 4))
+    crow = parts * cap_rows * Hq
+    list_cap = -(-T // 128) + E + parts * (-(-cap_rows // 128) + slots)
+    assert ws(pk.KV_EXTEND_AUTO) == (a256(4 * (4 + 2 * slots)) + a256(16 * list_cap) +
+                                     a256(crow * 128 * 4) + a256(crow * 4))
+    # a context within one chunk leaves nothing to split: plain fused
+    assert L.extend_attn_workspace_bytes_ex(ctypes.byref(c), E, T, Hq, chunk, budget,
+                                            pk.KV_EXTEND_AUTO) == 0
     assert ws(7) == 0                                 # invalid mode
 
 
