@@ -1012,7 +1012,6 @@ constexpr int kPlanHead = 4;
 constexpr int kHybridMaxSeqs = 1024;          // requests the plan takes
 constexpr int kHybridMaxSplit = 16;           // requests that may run split
 constexpr int64_t kHybridPartialBytes = 64ll << 20;
-constexpr int kListSortMax = 2048;            // longer lists keep request order
 struct ListEntry {
   int32_t seq, slot, part, qi;                // slot -1: fused
 };
@@ -1191,153 +1190,140 @@ __global__ __launch_bounds__(256) void extend_merge_kernel(AttnArgs a) {
   if (lane == 0 && a.lse) a.lse[rh] = M + __log2f(wsum) * kLn2;
 }
 
-// Plan of the hybrid extend (one workgroup).  A fused work item of request b
-// (n_b new tokens, C_b cached) with rows [i R, (i+1) R) walks ceil(C_b/64)
-// context tiles and ceil(min((i+1) R, n_b)/64) new-token tiles (R = 128 rows
-// for head pairs, 256 for two row tiles of one head); its longest item walks
-// walk_b = ceil(C_b/64) + ceil(n_b/64).  The batch's work, summed over every
-// item, spread over the resident workgroups gives the mean load D.  A request
-// with walk_b > D / 2 holds workgroups for a large part of the kernel's time
-// by itself, and late if they start late; if its context spans more than one
-// chunk it runs split (its chunks in parallel), while slots (max_split) and
-// compact partial rows (rows: the workspace holds n_parts x rows partials)
-// last, in request order.  Then the work list: every query item of a fused
-// request and every (part, query item) of a split one, with its walk as its
-// cost, sorted by request (heaviest request first) and within a request
-// heaviest first, when it has at most kListSortMax entries.
+// Exclusive prefix sum over the 1024 threads of a workgroup (v of thread t
+// -> sum of v over threads < t); *total gets the sum over all of them.
+__device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* s_tmp, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t inc = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(inc, off);
+    if (lane >= off) inc += u;
+  }
+  __syncthreads();                                        // s_tmp free
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int32_t base = 0, all = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int32_t x = s_tmp[i];
+    base += i < wave ? x : 0;
+    all += x;
+  }
+  *total = all;
+  return base + inc - v;
+}
+
+// Plan of the hybrid extend (one workgroup, one request per thread).  A fused
+// work item of request b (n_b new tokens, C_b cached) with rows [i R, (i+1) R)
+// walks ceil(C_b/64) context tiles and ceil(min((i+1) R, n_b)/64) new-token
+// tiles (R = 128 rows for head pairs, 256 for two row tiles of one head); its
+// longest item walks walk_b = ceil(C_b/64) + ceil(n_b/64).  The batch's work,
+// summed over every item, spread over the resident workgroups gives the mean
+// load D.  A request with walk_b > D / 2 holds workgroups for a large part of
+// the kernel's time by itself, and late if they start late; if its context
+// spans more than one chunk it is a candidate to run split (its chunks in
+// parallel), and candidates are taken in request order while the running
+// count stays within max_split and their running rows within the compact
+// partial rows (rows).  Then the work list: every query item of a fused
+// request and every (part, query item) of a split one, requests sorted by
+// their heaviest entry (heaviest first, ties in request order), each
+// request's entries heaviest first (context chunks before the new-token
+// part, later query items first).
 __global__ __launch_bounds__(1024) void extend_plan_kernel(AttnArgs a) {
-  __shared__ int32_t s_c[kHybridMaxSeqs], s_n[kHybridMaxSeqs], s_slot[kHybridMaxSeqs];
-  __shared__ int32_t s_off[kHybridMaxSeqs + 1];
+  __shared__ int32_t s_tmp[16];
   __shared__ int64_t s_w[16];
-  __shared__ int32_t s_wsum[16];
-  __shared__ uint64_t s_key[kListSortMax];
-  __shared__ ListEntry s_ent[kListSortMax];
+  __shared__ uint32_t s_key[kHybridMaxSeqs];
+  __shared__ int32_t s_cnt[kHybridMaxSeqs];
+  __shared__ int32_t s_slot[kHybridMaxSeqs];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t R = a.pairs ? kBM : 2 * kBM;
   int32_t* plan = (int32_t*)a.plan;
-  int64_t w = 0;
-  for (int32_t b = t; b < a.num_seqs; b += 1024) {
-    const int32_t n = a.cu[b + 1] - a.cu[b];
-    const int32_t C = context_len(a, b);
-    s_c[b] = C;
-    s_n[b] = n;
-    s_slot[b] = -1;
-    if (n > 0) {
-      const int64_t k = (n + R - 1) / R;                  // query items per lane
-      const int64_t ct = (C + kBN - 1) / kBN;
-      w += (int64_t)a.Hkv * a.Gs * (k * ct + (R / kBN) * (k - 1) * k / 2 + (n + kBN - 1) / kBN);
-    }
-  }
+  const bool mine = t < a.num_seqs;
+  const int32_t n = mine ? a.cu[t + 1] - a.cu[t] : 0;
+  const int32_t C = mine ? context_len(a, t) : 0;
+  const int32_t k = (n + R - 1) / R;                      // query items per lane
+  const int32_t ct = (C + kBN - 1) / kBN, nt = (n + kBN - 1) / kBN;
+  int64_t w = n > 0 ? (int64_t)a.Hkv * a.Gs * ((int64_t)k * ct + (R / kBN) * (int64_t)(k - 1) * k / 2 + nt)
+                    : 0;
   for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
   if (lane == 0) s_w[wave] = w;
   __syncthreads();
-  if (t == 0) {
-    int64_t tot = 0;
-    for (int i = 0; i < 16; ++i) tot += s_w[i];
-    const int64_t D = tot / (a.plan_slots > 0 ? a.plan_slots : 1);
-    int32_t n_split = 0, used = 0;
-    for (int32_t b = 0; b < a.num_seqs && n_split < a.max_split; ++b) {
-      const int32_t C = s_c[b], n = s_n[b];
-      const int64_t walk = (C + kBN - 1) / kBN + (n + kBN - 1) / kBN;
-      if (n > 0 && 2 * walk > D && C > a.chunk_tokens && used + n <= a.rows) {
-        plan[kPlanHead + n_split] = b;
-        plan[kPlanHead + a.max_split + n_split] = used;
-        s_slot[b] = n_split;
-        used += n;
-        ++n_split;
-      }
-    }
-    plan[0] = n_split;
-    plan[1] = used;
+  int64_t tot = 0;
+  for (int i = 0; i < 16; ++i) tot += s_w[i];
+  const int64_t D = tot / (a.plan_slots > 0 ? a.plan_slots : 1);
+  // split candidates, taken in request order while slots and rows last
+  const bool cand = n > 0 && 2 * (int64_t)(ct + nt) > D && C > a.chunk_tokens;
+  int32_t all_c, all_r;
+  const int32_t before_c = block_scan_1024(cand ? 1 : 0, s_tmp, &all_c);
+  const int32_t before_r = block_scan_1024(cand ? n : 0, s_tmp, &all_r);
+  const bool split = cand && before_c < a.max_split && before_r + n <= a.rows;
+  int32_t n_split, used;
+  const int32_t slot_of = block_scan_1024(split ? 1 : 0, s_tmp, &n_split);
+  const int32_t row_off = block_scan_1024(split ? n : 0, s_tmp, &used);
+  const int32_t slot = split ? slot_of : -1;
+  if (split) {
+    plan[kPlanHead + slot] = t;
+    plan[kPlanHead + a.max_split + slot] = row_off;
   }
-  __syncthreads();
-  // entries per request (one request per thread) and their exclusive offsets
-  int32_t cnt = 0;
-  if (t < a.num_seqs && s_n[t] > 0) {
-    const int32_t k = (s_n[t] + R - 1) / R;
-    int32_t np = 1 + (s_c[t] + a.chunk_tokens - 1) / a.chunk_tokens;
-    np = np > a.n_parts ? a.n_parts : np;
-    cnt = s_slot[t] < 0 ? k : np * k;
-  }
-  int32_t inc = cnt;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t v = __shfl_up(inc, off);
-    if (lane >= off) inc += v;
-  }
-  if (lane == 63) s_wsum[wave] = inc;
-  __syncthreads();
-  int32_t base = 0;
-  for (int i = 0; i < wave; ++i) base += s_wsum[i];
-  if (t < a.num_seqs) s_off[t] = base + inc - cnt;
-  if (t == 1023) s_off[a.num_seqs] = base + inc;
-  __syncthreads();
-  const int32_t total = s_off[a.num_seqs];
-  const int32_t E = total < a.list_cap ? total : a.list_cap;
-  const bool sorted = E <= kListSortMax;
-  ListEntry* list = (ListEntry*)a.list;
-  if (cnt > 0) {
-    const int32_t n = s_n[t], C = s_c[t], slot = s_slot[t];
-    const int32_t k = (n + R - 1) / R;
-    const int32_t ct = (C + kBN - 1) / kBN;
-    // the request's heaviest entry: its last query item (fused), else its
-    // last query item of the new tokens or a whole chunk (split)
-    const int32_t nt = (n + kBN - 1) / kBN;
-    const int32_t cht = ((C < a.chunk_tokens ? C : a.chunk_tokens) + kBN - 1) / kBN;
-    const int32_t rcost = slot < 0 ? ct + nt : (nt > cht ? nt : cht);
-    const uint64_t rkey = ((uint64_t)(0xFFFFu - (uint32_t)(rcost < 0xFFFF ? rcost : 0xFFFF)) << 48) |
-                          ((uint64_t)t << 32);
-    for (int32_t i = 0; i < cnt; ++i) {
-      const int32_t idx = s_off[t] + i;
-      if (idx >= E) break;
-      ListEntry e;
-      int32_t cost;
-      e.seq = t;
-      e.slot = slot;
-      e.qi = i % k;
-      e.part = slot < 0 ? 0 : i / k;
-      const int32_t rows_to = min((e.qi + 1) * R, n);
-      if (slot < 0) {
-        cost = ct + (rows_to + kBN - 1) / kBN;
-      } else if (e.part == 0) {
-        cost = (rows_to + kBN - 1) / kBN;
-      } else {
-        const int32_t left = C - (e.part - 1) * a.chunk_tokens;
-        cost = ((left < a.chunk_tokens ? left : a.chunk_tokens) + kBN - 1) / kBN;
-      }
-      if (sorted) {
-        // requests heaviest first, each request's entries heaviest first:
-        // the lanes of a request run together and share its K/V in L2
-        s_ent[idx] = e;
-        const uint64_t c16 = (uint64_t)(cost < 0xFFFF ? cost : 0xFFFF);
-        s_key[idx] = rkey | ((0xFFFFull - c16) << 11) | (uint64_t)idx;
-      } else {
-        list[idx] = e;
-      }
+  // entries and the request order
+  int32_t np = 1 + (C + a.chunk_tokens - 1) / a.chunk_tokens;
+  np = np > a.n_parts ? a.n_parts : np;
+  const int32_t cnt = n == 0 ? 0 : (slot < 0 ? k : np * k);
+  const int32_t cht = ((C < a.chunk_tokens ? C : a.chunk_tokens) + kBN - 1) / kBN;
+  const int32_t rcost = slot < 0 ? ct + nt : (nt > cht ? nt : cht);
+  int32_t N = 1;
+  while (N < a.num_seqs) N <<= 1;
+  if (t < N) {
+    s_key[t] = cnt > 0 ? ((0xFFFFu - (uint32_t)(rcost < 0xFFFF ? rcost : 0xFFFF)) << 10) | (uint32_t)t
+                       : 0xFFFFFFFFu;
+    if (mine) {
+      s_cnt[t] = cnt;
+      s_slot[t] = slot;
     }
   }
-  if (sorted) {
-    int32_t N = 2;
-    while (N < E) N <<= 1;
-    for (int32_t i = E + t; i < N; i += 1024) s_key[i] = ~0ull;
-    __syncthreads();
-    for (int32_t kk = 2; kk <= N; kk <<= 1) {
-      for (int32_t jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int32_t i = t; i < N; i += 1024) {
-          const int32_t ixj = i ^ jj;
-          if (ixj > i) {
-            const uint64_t x = s_key[i], y = s_key[ixj];
-            if ((x > y) == ((i & kk) == 0)) {
-              s_key[i] = y;
-              s_key[ixj] = x;
-            }
+  __syncthreads();
+  for (int32_t kk = 2; kk <= N; kk <<= 1) {
+    for (int32_t jj = kk >> 1; jj > 0; jj >>= 1) {
+      if (t < N) {
+        const int32_t ixj = t ^ jj;
+        if (ixj > t) {
+          const uint32_t x = s_key[t], y = s_key[ixj];
+          if ((x > y) == ((t & kk) == 0)) {
+            s_key[t] = y;
+            s_key[ixj] = x;
           }
         }
-        __syncthreads();
       }
+      __syncthreads();
     }
-    for (int32_t i = t; i < E; i += 1024) list[i] = s_ent[s_key[i] & 0x7FFull];
   }
-  if (t == 0) plan[2] = E;
+  // thread t writes the entries of the request at sorted position t
+  const uint32_t key = t < N ? s_key[t] : 0xFFFFFFFFu;
+  const int32_t b = key != 0xFFFFFFFFu ? (int32_t)(key & 0x3FFu) : -1;
+  const int32_t bcnt = b >= 0 ? s_cnt[b] : 0;
+  int32_t total;
+  const int32_t off = block_scan_1024(bcnt, s_tmp, &total);
+  const int32_t E = total < a.list_cap ? total : a.list_cap;
+  if (bcnt > 0) {
+    ListEntry* list = (ListEntry*)a.list;
+    const int32_t bn = a.cu[b + 1] - a.cu[b];
+    const int32_t bk = (bn + R - 1) / R;
+    const int32_t bslot = s_slot[b];
+    const int32_t bparts = bcnt / bk;
+    for (int32_t i = 0; i < bcnt && off + i < E; ++i) {
+      ListEntry e;
+      e.seq = b;
+      e.slot = bslot;
+      e.qi = bk - 1 - i % bk;                             // later query items first
+      const int32_t pi = i / bk;                          // context chunks first, new tokens last
+      e.part = bslot < 0 ? 0 : (pi + 1 < bparts ? pi + 1 : 0);
+      list[off + i] = e;
+    }
+  }
+  if (t == 0) {
+    plan[0] = n_split;
+    plan[1] = used;
+    plan[2] = E;
+  }
 }
 
 // Merge of the hybrid extend's split requests: one wave per compact (row,
