@@ -4,10 +4,10 @@ paths", extend path: (1) the new tokens among themselves, (2) all new tokens
 against each chunk of the cached context, (3) the log-sum-exp merge; section
 "Why route three ways explicitly": extend batches mix long and short
 requests).  In automatic mode, when the fused execution is chosen and the
-context spans two or more chunks, a device-side plan runs the requests whose
-walk would hold their workgroups far beyond the batch's mean load split --
-their chunks in parallel, partials merged -- beside the fused requests in the
-same launch.
+context spans two or more chunks, a device-side plan lists every query item
+of the batch (requests heaviest first) and runs the requests whose walk would
+hold their workgroups far beyond the batch's mean load split -- their chunks
+in parallel, partials merged -- beside the fused requests in the same launch.
 
 Checks: the plan (white box: the first two words of the workspace are the
 number of split requests and the compact rows they use) splits the expected
@@ -40,6 +40,9 @@ CASES = [
     ("64:4 fp8 nhd", 64, 4, ONE_LONG_CTX, ONE_LONG_NEW, 32768, "nhd", "fp8", [0]),
     ("64:4 fp8 preshuffled", 64, 4, ONE_LONG_CTX, ONE_LONG_NEW, 32768, "preshuffled", "fp8", [0]),
     ("64:4 bf16 preshuffled", 64, 4, ONE_LONG_CTX, ONE_LONG_NEW, 32768, "preshuffled", "bf16", [0]),
+    # four lanes only (fewer than the XCDs): one long request beside a
+    # 16000-token extend that alone fills the GPU
+    ("8:2 few lanes", 8, 2, [30000, 100, 200], [20, 16000, 500], 8192, "nhd", "bf16", [0]),
 ]
 
 
