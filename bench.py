@@ -59,7 +59,9 @@ step on the stream the library launches on.  traffic: HBM bytes per
 call from rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by what the same
 counters read for the pack kernel (a plain copy of known size), read from the
 committed profile when it was taken on the current kernel sources, else null.
-cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
+(for the decode layer and the tiny decode also with its BLAS on one thread,
+"one_thread").
 """
 from __future__ import annotations
 
@@ -78,6 +80,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 SETTLE_S = 0.25                # untimed sustained work before each workload's warm-up
+ONE_THREAD_BASELINE = ("llama70b_decode_layer", "tiny_decode")   # oracle also timed on one thread
 SETTLE_MAX_STEPS = 2000
 
 METRIC = "paged decode HBM GB/s (% of 8 TB/s); mixed-batch attention tokens/s"
@@ -854,6 +857,15 @@ def main():
             cpu = {"value": round(v, 4), "unit": unit, "cores": info["blas_threads"],
                    "kind": "oracle", "sample": sample, "precision": "float64",
                    "cpu_model": info["cpu_model"], "os_cpu_count": info["os_cpu_count"]}
+            if name in ONE_THREAD_BASELINE:
+                # the same oracle with its BLAS limited to one thread
+                try:
+                    from threadpoolctl import threadpool_limits
+                    with threadpool_limits(limits=1):
+                        v1, sample1 = cpu_sample(args.cpu_budget * 0.3)
+                    cpu["one_thread"] = {"value": round(v1, 4), "cores": 1, "sample": sample1}
+                except ImportError:
+                    cpu["one_thread"] = None
         hev.close()
         # free this workload's device memory before the next one
         del calls, extra, built
