@@ -160,6 +160,26 @@ def test_prefill_persistent_walk(causal, Hq, Hkv):
     assert not np.isnan(out).any()
 
 
+def test_prefill_walk_mostly_empty_rounds():
+    """299 one-token prompts beside one of 131072 tokens, 8:2 heads: every
+    request gets as many query items as the longest (1024), so a persistent
+    workgroup walks ~4800 rounds, nearly all of them empty and skipped.  Every
+    short row and sampled rows of the long prompt against the oracle."""
+    lens = [1] * 299 + [131072]
+    say("prefill 299 x 1 + 1 x 131072 tokens, 8:2, causal")
+    cu, q, k, v, out, lse = _prefill(lens, 8, 2, True, 48)
+    n = lens[-1]
+    s0 = int(cu[-2])
+    rng = np.random.default_rng(8)
+    rows = list(range(299)) + sorted({s0, s0 + 1, s0 + 127, s0 + 128, s0 + n - 1}
+                                     | {s0 + int(x) for x in rng.integers(0, n, 12)})
+    ro, rl = oa.prefill(ob.to_f64(q), ob.to_f64(k), ob.to_f64(v), cu, SCALE, True, rows=rows)
+    e = max_err(out[rows], ro[rows])
+    el = max_err(lse[rows], rl[rows])
+    say(f"  max|err| out {e:.3e} lse {el:.3e} over {len(rows)} rows")
+    assert e <= BF16_TOL and el <= LSE_TOL
+
+
 @pytest.mark.parametrize("bs", [1, 16, 32])
 def test_extend_fused_ragged_contexts(bs):
     """Enough query tiles for the fused extend (64 heads x 17 query tiles),
