@@ -83,6 +83,12 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m paged_kv_cache_mapped_amd.build` (no fallback exists)")
+        # torch first: its wheel carries its own HIP runtime (soname
+        # libamdhip64.so.7).  Loaded after it, the library binds to that same
+        # runtime; loaded before it, the library would pull the system's copy
+        # and the process would hold two runtimes, whose devices, streams and
+        # allocations are not each other's (the library's calls then fail).
+        _t()
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)

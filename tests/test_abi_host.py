@@ -275,3 +275,22 @@ def test_binding_refuses_tensors_the_abi_would_misread():
     with pytest.raises(ValueError, match="GPU"):      # right types, but host memory
         pk.PagedKVCache(torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16),
                         torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16), 16, 8, 128)
+
+
+def test_library_shares_torchs_hip_runtime_when_loaded_first():
+    """A host-only call (here the batch reorder) before any torch import must
+    not give the process a second HIP runtime: the library has to bind to the
+    one that owns torch's devices, streams and allocations."""
+    import subprocess
+    import sys
+    code = (
+        "import paged_kv_cache_mapped_amd as pk\n"
+        "pk.reorder_batch([1, 5], [3, 0])\n"
+        "import torch\n"
+        "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+        "print(len(paths))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[-1] == "1", r.stdout
