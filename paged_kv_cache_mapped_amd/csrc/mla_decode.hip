@@ -125,10 +125,12 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(MlaArgs a) {
 // One copy instruction of a tile: 64 lanes x 16 bytes from sbase + voff into
 // the 1 KB of LDS at lds (lane i at lds + 16 i).  m0 is saved and restored
 // around it (a reserved register the compiler may not list as clobbered).
+// Every latent row is read once per call, so the copy is non-temporal (`nt`):
+// the rows stream past the caches instead of filling L2.
 __device__ __forceinline__ void copy16(uint32_t lds, uint32_t voff, const void* sbase) {
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds), "v"(voff), "s"(sbase)
