@@ -99,6 +99,28 @@ __device__ __forceinline__ int dmap(int kk, int q4) {
   else return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
 }
 
+// Token (relative to the tile start) of row rr of K subtile s, and of element
+// i of a lane's score accumulator s in lane quarter q4 (its accumulator rows
+// are 4 q4 .. 4 q4 + 3); the score of that token is probability k-slot
+// 4 s + i of the lane's P^T fragment.  Default: k-slots 8 q4 .. 8 q4 + 7 are
+// tokens 8 q4 .. 8 q4 + 7 of the tile.  The fp8 preshuffled cache stores 16
+// consecutive tokens of one 16-dim chunk contiguously (16 bytes each), so
+// there each subtile takes 8 consecutive tokens from each 16-token half of
+// the tile -- every K load instruction then reads whole 128-byte lines --
+// and lane quarter q4 ends up with tokens of half q4 / 2 only.
+template <int LAYOUT, int DT>
+__device__ __forceinline__ int k_row_token(int s, int rr) {
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_FP8_E4M3)
+    return 16 * (rr >> 3) + 8 * s + (rr & 7);
+  else return 8 * (rr >> 2) + 4 * s + (rr & 3);
+}
+template <int LAYOUT, int DT>
+__device__ __forceinline__ int score_token(int q4, int s, int i) {
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_FP8_E4M3)
+    return 16 * (q4 >> 1) + 8 * s + 4 * (q4 & 1) + i;
+  else return 8 * q4 + 4 * s + i;
+}
+
 // K/V bytes are read once per call: non-temporal loads (the `nt` cache
 // policy) stream them past the caches instead of filling L2 with lines that
 // are never read again, which lets the decode's loads reach a higher rate.
@@ -121,10 +143,10 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
                                            int hkv, int32_t t0, int32_t t_end, int lane,
                                            TileRaw& R) {
   const int q4 = lane >> 4, r = lane & 15;
-  // K: A-operand rows = tokens t0 + 8*(r/4) + 4*s + r%4 (subtile s)
+  // K: A-operand row r of subtile s = token t0 + k_row_token(s, r)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int32_t tok = min(t0 + 8 * (r >> 2) + 4 * s + (r & 3), t_end - 1);
+    const int32_t tok = min(t0 + k_row_token<LAYOUT, DT>(s, r), t_end - 1);
     const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
     const int32_t off = tok & (a.bs - 1);
     if constexpr (LAYOUT == KV_LAYOUT_NHD) {
@@ -254,33 +276,34 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
 #pragma unroll
       for (int n = 0; n < 8; ++n) va[n] = __builtin_bit_cast(bf16x8_t, R.v[n]);
     } else {
-      // Load j of lane (q4, r) holds tokens [lo | hi] = [16 (q4/2) .. +7 |
-      // +8 .. +15] of dim 16 (2 j + q4 % 2) + r.  Swapping lo of the odd rows
-      // of 16 lanes with hi of the even rows leaves, in every lane, lo = dim
-      // 16 (2 j) + r and hi = dim 16 (2 j + 1) + r, both for tokens
-      // 8 q4 .. 8 q4 + 7 (v_permlane16_swap_b32: odd rows of the first
+      // Load j of lane (q4, r) holds the 16 tokens of tile half q4 / 2 of dim
+      // 16 (2 j + q4 % 2) + r as words w0..w3 (4 tokens each).  The lane's
+      // P^T k-slots are tokens {0-3, 8-11} (even q4) or {4-7, 12-15} (odd q4)
+      // of that half: words 0 and 2, or 1 and 3.  Swapping w0 of the odd rows
+      // of 16 lanes with w1 of the even rows, and w2 with w3, leaves in every
+      // lane (w0, w2) of dim 16 (2 j) + r and (w1, w3) of dim 16 (2 j + 1) + r
+      // for exactly those tokens (v_permlane16_swap_b32: odd rows of the first
       // operand <-> even rows of the second).
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t l0 = R.v[j][0], l1 = R.v[j][1], h0 = R.v[j][2], h1 = R.v[j][3];
+        uint32_t w0 = R.v[j][0], w1 = R.v[j][1], w2 = R.v[j][2], w3 = R.v[j][3];
         asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
-                     : "+v"(l0), "+v"(h0), "+v"(l1), "+v"(h1));
-        va[2 * j] = fp8x8_to_bf16(u32x2_t{l0, l1});
-        va[2 * j + 1] = fp8x8_to_bf16(u32x2_t{h0, h1});
+                     : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3));
+        va[2 * j] = fp8x8_to_bf16(u32x2_t{w0, w2});
+        va[2 * j + 1] = fp8x8_to_bf16(u32x2_t{w1, w3});
       }
     }
     if (partial) {
-      const int32_t tv = t0 + 8 * q4;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        if (tv + jj >= t_end) {
+        if (t0 + score_token<LAYOUT, DT>(q4, jj >> 2, jj & 3) >= t_end) {
 #pragma unroll
           for (int n = 0; n < 8; ++n) va[n][jj] = (__bf16)0.f;
         }
     }
   }
 
-  // ---- S^T = K Q^T: element i of acc[s] is token t0 + 8*q4 + 4*s + i, head r
+  // ---- S^T = K Q^T: element i of acc[s] is token t0 + score_token(q4, s, i), head r
   f32x4_t acc[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -293,7 +316,7 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int32_t tok = t0 + 8 * q4 + 4 * s + i;
+      const int32_t tok = t0 + score_token<LAYOUT, DT>(q4, s, i);
       sc[4 * s + i] = (partial && tok >= t_end) ? kNegInf : acc[s][i] * a.qk_mult;
     }
 
