@@ -143,23 +143,32 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
                                            int hkv, int32_t t0, int32_t t_end, int lane,
                                            TileRaw& R) {
   const int q4 = lane >> 4, r = lane & 15;
+  if constexpr (LAYOUT == KV_LAYOUT_NHD && DT == KV_DTYPE_BF16) {
+    // K and V rows of token t0 + 4 j + lane / 16, 16-byte chunk lane % 16:
+    // every load instruction reads four whole 256-byte rows (K reaches the
+    // MFMA layout through LDS in consume_tile)
+    const int a4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int32_t tok = min(t0 + 4 * j + a4, t_end - 1);
+      const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+      const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
+      R.k[j] = stream_load((const u32x4_t*)(a.kc + row * (kD * 2) + c16 * 16));
+      R.v[j] = stream_load((const u32x4_t*)(a.vc + row * (kD * 2) + c16 * 16));
+    }
+    return;
+  }
   // K: A-operand row r of subtile s = token t0 + k_row_token(s, r)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int32_t tok = min(t0 + k_row_token<LAYOUT, DT>(s, r), t_end - 1);
     const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
     const int32_t off = tok & (a.bs - 1);
-    if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    if constexpr (LAYOUT == KV_LAYOUT_NHD) {                  // fp8
       const int64_t row = ((int64_t)blk * a.bs + off) * a.Hkv + hkv;
-      if constexpr (DT == KV_DTYPE_BF16) {
-        const uint8_t* p = a.kc + row * (kD * 2);
+      const uint8_t* p = a.kc + row * kD;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) R.k[4 * s + kk] = stream_load((const u32x4_t*)(p + dmap<DT>(kk, q4) * 2));
-      } else {
-        const uint8_t* p = a.kc + row * kD;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) R.k[2 * s + pp] = stream_load((const u32x4_t*)(p + 16 * (4 * pp + q4)));
-      }
+      for (int pp = 0; pp < 2; ++pp) R.k[2 * s + pp] = stream_load((const u32x4_t*)(p + 16 * (4 * pp + q4)));
     } else {
       const int64_t bh = (int64_t)blk * a.Hkv + hkv;
       if constexpr (DT == KV_DTYPE_BF16) {   // [blk][h][D/8][bs][8]
@@ -177,20 +186,11 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
       }
     }
   }
-  // V: NHD rows as 16-byte chunks of whole rows (bf16: row 4*j4 + lane/16,
-  // chunk lane%16; fp8: row 8*j + lane/8, chunk lane%8); preshuffled V as the
-  // V^T operand (bf16: 8 tokens of dim 16n + r; fp8: see below).
+  // V: NHD fp8 rows as 16-byte chunks of whole rows (row 8*j + lane/8, chunk
+  // lane%8); preshuffled V as the V^T operand (bf16: 8 tokens of dim 16n + r;
+  // fp8: see below).
   if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-    if constexpr (DT == KV_DTYPE_BF16) {
-      const int a4 = lane >> 4, c16 = lane & 15;
-#pragma unroll
-      for (int j4 = 0; j4 < 8; ++j4) {
-        const int32_t tok = min(t0 + 4 * j4 + a4, t_end - 1);
-        const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
-        const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
-        R.v[j4] = stream_load((const u32x4_t*)(a.vc + row * (kD * 2) + c16 * 16));
-      }
-    } else {
+    {
       const int a8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -240,17 +240,42 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
   const int q4 = lane >> 4, r = lane & 15;
   const bool partial = t0 + kTile > t_end;
   bf16x8_t ka[2][4];
+  if constexpr (LAYOUT == KV_LAYOUT_NHD && DT == KV_DTYPE_BF16) {
+    // K rows into the wave's LDS slice (256-byte rows, 16-byte chunk c of row
+    // x at position c ^ kfold(x)), then the A-operand fragments out: row
+    // 8 (r / 4) + 4 s + r % 4, chunk 4 kk + q4.  kfold differs between the 16
+    // rows of one fragment read and permutes the chunks of each row written,
+    // so neither access pattern has bank conflicts.  The V rows written next
+    // reuse the slice; one wave's LDS requests are served in order.
+    auto kfold = [](int x) { return (x & 3) | (((x >> 3) & 3) << 2); };
+    const int a4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if constexpr (DT == KV_DTYPE_BF16) {
+    for (int j = 0; j < 8; ++j) {
+      const int x = 4 * j + a4;
+      *(u32x4_t*)(vt + x * 256 + 16 * (c16 ^ kfold(x))) = R.k[j];
+    }
+    order_lds();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[s][kk] = __builtin_bit_cast(bf16x8_t, R.k[4 * s + kk]);
-    } else {
+    for (int s = 0; s < 2; ++s) {
+      const int x = 8 * (r >> 2) + 4 * s + (r & 3);
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const u32x4_t w = R.k[2 * s + pp];
-        ka[s][2 * pp] = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
-        ka[s][2 * pp + 1] = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+      for (int kk = 0; kk < 4; ++kk)
+        ka[s][kk] = *(const bf16x8_t*)(vt + x * 256 + 16 * ((4 * kk + q4) ^ kfold(x)));
+    }
+    order_lds();
+  } else {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if constexpr (DT == KV_DTYPE_BF16) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[s][kk] = __builtin_bit_cast(bf16x8_t, R.k[4 * s + kk]);
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const u32x4_t w = R.k[2 * s + pp];
+          ka[s][2 * pp] = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
+          ka[s][2 * pp + 1] = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+        }
       }
     }
   }
