@@ -103,21 +103,19 @@ __device__ __forceinline__ int dmap(int kk, int q4) {
 // i of a lane's score accumulator s in lane quarter q4 (its accumulator rows
 // are 4 q4 .. 4 q4 + 3); the score of that token is probability k-slot
 // 4 s + i of the lane's P^T fragment.  Default: k-slots 8 q4 .. 8 q4 + 7 are
-// tokens 8 q4 .. 8 q4 + 7 of the tile.  The fp8 preshuffled cache stores 16
-// consecutive tokens of one 16-dim chunk contiguously (16 bytes each), so
-// there each subtile takes 8 consecutive tokens from each 16-token half of
-// the tile -- every K load instruction then reads whole 128-byte lines --
-// and lane quarter q4 ends up with tokens of half q4 / 2 only.
+// tokens 8 q4 .. 8 q4 + 7 of the tile.  The preshuffled K cache stores the
+// tokens of a block consecutively for each 16-byte dim chunk, so there each
+// subtile takes 8 consecutive tokens from each 16-token half of the tile --
+// every K load instruction then reads whole 128-byte lines -- and lane
+// quarter q4 ends up with tokens of half q4 / 2 only.
 template <int LAYOUT, int DT>
 __device__ __forceinline__ int k_row_token(int s, int rr) {
-  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_FP8_E4M3)
-    return 16 * (rr >> 3) + 8 * s + (rr & 7);
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (rr >> 3) + 8 * s + (rr & 7);
   else return 8 * (rr >> 2) + 4 * s + (rr & 3);
 }
 template <int LAYOUT, int DT>
 __device__ __forceinline__ int score_token(int q4, int s, int i) {
-  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_FP8_E4M3)
-    return 16 * (q4 >> 1) + 8 * s + 4 * (q4 & 1) + i;
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (q4 >> 1) + 8 * s + 4 * (q4 & 1) + i;
   else return 8 * q4 + 4 * s + i;
 }
 
@@ -298,8 +296,18 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
     }
   } else {
     if constexpr (DT == KV_DTYPE_BF16) {
+      // Load n of lane (q4, r) holds tokens 8 q4 .. 8 q4 + 7 of dim 16 n + r,
+      // two per word.  The lane's P^T k-slots are tokens 0-3 (even q4) or
+      // 4-7 (odd q4) of 8-token groups q4 & ~1 and q4 | 1: swapping (w0, w1)
+      // of the odd rows of 16 lanes with (w2, w3) of the even rows leaves
+      // exactly those, in k-slot order.
 #pragma unroll
-      for (int n = 0; n < 8; ++n) va[n] = __builtin_bit_cast(bf16x8_t, R.v[n]);
+      for (int n = 0; n < 8; ++n) {
+        uint32_t w0 = R.v[n][0], w1 = R.v[n][1], w2 = R.v[n][2], w3 = R.v[n][3];
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+                     : "+v"(w0), "+v"(w2), "+v"(w1), "+v"(w3));
+        va[n] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0, w1, w2, w3});
+      }
     } else {
       // Load j of lane (q4, r) holds the 16 tokens of tile half q4 / 2 of dim
       // 16 (2 j + q4 % 2) + r as words w0..w3 (4 tokens each).  The lane's
