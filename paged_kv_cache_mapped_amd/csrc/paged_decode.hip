@@ -90,13 +90,15 @@ __device__ __forceinline__ int32_t clamp_block(int32_t blk, int32_t nb) {
   return blk < 0 ? 0 : (blk >= nb ? nb - 1 : blk);
 }
 
-// Query dims held by lane quarter q4 for MFMA k-step kk.  bf16 caches use the
-// natural order; fp8 caches hand each lane 16 consecutive dims per load, i.e.
-// k-steps 2p and 2p+1 read one 16-dim chunk 4p + q4.
-template <int DT>
+// Query dims held by lane quarter q4 for MFMA k-step kk.  Natural order where
+// the K fragments come as bf16 (bf16 caches, and NHD fp8 whose K is decoded
+// into LDS rows); the preshuffled fp8 cache hands each lane 16 consecutive
+// dims per load, i.e. k-steps 2p and 2p+1 read one 16-dim chunk 4p + q4.
+template <int LAYOUT, int DT>
 __device__ __forceinline__ int dmap(int kk, int q4) {
-  if constexpr (DT == KV_DTYPE_BF16) return 32 * kk + 8 * q4;
-  else return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_FP8_E4M3)
+    return 64 * (kk >> 1) + 16 * q4 + 8 * (kk & 1);
+  else return 32 * kk + 8 * q4;
 }
 
 // Token (relative to the tile start) of row rr of K subtile s, and of element
@@ -156,53 +158,47 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
     }
     return;
   }
-  // K: A-operand row r of subtile s = token t0 + k_row_token(s, r)
+  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    // fp8: K and V rows of token t0 + 8 j + lane / 8, 16-byte chunk lane % 8
+    // (eight whole 128-byte rows per instruction)
+    const int a8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t tok = min(t0 + 8 * j + a8, t_end - 1);
+      const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
+      const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
+      R.k[j] = stream_load((const u32x4_t*)(a.kc + row * kD + c8 * 16));
+      R.v[j] = stream_load((const u32x4_t*)(a.vc + row * kD + c8 * 16));
+    }
+    return;
+  }
+  // Preshuffled K: A-operand row r of subtile s = token t0 + k_row_token(s, r)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int32_t tok = min(t0 + k_row_token<LAYOUT, DT>(s, r), t_end - 1);
     const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
     const int32_t off = tok & (a.bs - 1);
-    if constexpr (LAYOUT == KV_LAYOUT_NHD) {                  // fp8
-      const int64_t row = ((int64_t)blk * a.bs + off) * a.Hkv + hkv;
-      const uint8_t* p = a.kc + row * kD;
+    const int64_t bh = (int64_t)blk * a.Hkv + hkv;
+    if constexpr (DT == KV_DTYPE_BF16) {     // [blk][h][D/8][bs][8]
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) R.k[2 * s + pp] = stream_load((const u32x4_t*)(p + 16 * (4 * pp + q4)));
-    } else {
-      const int64_t bh = (int64_t)blk * a.Hkv + hkv;
-      if constexpr (DT == KV_DTYPE_BF16) {   // [blk][h][D/8][bs][8]
+      for (int kk = 0; kk < 4; ++kk) {
+        const int64_t e = ((bh * (kD / 8) + (4 * kk + q4)) * a.bs + off) * 8;
+        R.k[4 * s + kk] = stream_load((const u32x4_t*)(a.kc + e * 2));
+      }
+    } else {                                  // [blk][h][D/16][bs][16]
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int64_t e = ((bh * (kD / 8) + (4 * kk + q4)) * a.bs + off) * 8;
-          R.k[4 * s + kk] = stream_load((const u32x4_t*)(a.kc + e * 2));
-        }
-      } else {                                // [blk][h][D/16][bs][16]
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int64_t e = ((bh * (kD / 16) + (4 * pp + q4)) * a.bs + off) * 16;
-          R.k[2 * s + pp] = stream_load((const u32x4_t*)(a.kc + e));
-        }
+      for (int pp = 0; pp < 2; ++pp) {
+        const int64_t e = ((bh * (kD / 16) + (4 * pp + q4)) * a.bs + off) * 16;
+        R.k[2 * s + pp] = stream_load((const u32x4_t*)(a.kc + e));
       }
     }
   }
-  // V: NHD fp8 rows as 16-byte chunks of whole rows (row 8*j + lane/8, chunk
-  // lane%8); preshuffled V as the V^T operand (bf16: 8 tokens of dim 16n + r;
-  // fp8: see below).
-  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
-    {
-      const int a8 = lane >> 3, c8 = lane & 7;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int32_t tok = min(t0 + 8 * j + a8, t_end - 1);
-        const int32_t blk = s_tab[(tok >> a.bs_log2) - ib0];
-        const int64_t row = ((int64_t)blk * a.bs + (tok & (a.bs - 1))) * a.Hkv + hkv;
-        R.v[j] = stream_load((const u32x4_t*)(a.vc + row * kD + c8 * 16));
-      }
-    }
-  } else if constexpr (DT == KV_DTYPE_FP8_E4M3) {
-    // 16-byte loads: lane (q4, r), load j takes the 16 tokens of block half
-    // q4 / 2 of the tile for dim 16 (2 j + q4 % 2) + r; consume_tile trades
-    // halves between lanes q4 and q4 ^ 1 so that each ends with tokens
-    // 8 q4 .. 8 q4 + 7 of dims 16 (2 j) + r and 16 (2 j + 1) + r.
+  // V as the V^T operand (bf16: 8 tokens of dim 16n + r; fp8: see below).
+  if constexpr (DT == KV_DTYPE_FP8_E4M3) {
+    // 16-byte loads: lane (q4, r), load j takes the 16 tokens of tile half
+    // q4 / 2 for dim 16 (2 j + q4 % 2) + r; consume_tile trades words between
+    // lanes q4 and q4 ^ 1 so that each ends with its P^T tokens of dims
+    // 16 (2 j) + r and 16 (2 j + 1) + r.
     const int32_t tb = min(t0 + 16 * (q4 >> 1), (t_end - 1) & ~15);   // aligned to 16
     const int32_t blk = s_tab[(tb >> a.bs_log2) - ib0];
     const int32_t off = tb & (a.bs - 1);
@@ -238,19 +234,31 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
   const int q4 = lane >> 4, r = lane & 15;
   const bool partial = t0 + kTile > t_end;
   bf16x8_t ka[2][4];
-  if constexpr (LAYOUT == KV_LAYOUT_NHD && DT == KV_DTYPE_BF16) {
-    // K rows into the wave's LDS slice (256-byte rows, 16-byte chunk c of row
-    // x at position c ^ kfold(x)), then the A-operand fragments out: row
-    // 8 (r / 4) + 4 s + r % 4, chunk 4 kk + q4.  kfold differs between the 16
-    // rows of one fragment read and permutes the chunks of each row written,
-    // so neither access pattern has bank conflicts.  The V rows written next
-    // reuse the slice; one wave's LDS requests are served in order.
+  if constexpr (LAYOUT == KV_LAYOUT_NHD) {
+    // K rows (fp8 decoded) as bf16 into the wave's LDS slice (256-byte rows,
+    // 16-byte chunk c of row x at position c ^ kfold(x)), then the A-operand
+    // fragments out: row 8 (r / 4) + 4 s + r % 4, chunk 4 kk + q4.  kfold
+    // differs between the 16 rows of one fragment read and permutes the
+    // chunks of each row written, so neither access pattern has bank
+    // conflicts.  The V rows written next reuse the slice; one wave's LDS
+    // requests are served in order.
     auto kfold = [](int x) { return (x & 3) | (((x >> 3) & 3) << 2); };
-    const int a4 = lane >> 4, c16 = lane & 15;
+    if constexpr (DT == KV_DTYPE_BF16) {
+      const int a4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int x = 4 * j + a4;
-      *(u32x4_t*)(vt + x * 256 + 16 * (c16 ^ kfold(x))) = R.k[j];
+      for (int j = 0; j < 8; ++j) {
+        const int x = 4 * j + a4;
+        *(u32x4_t*)(vt + x * 256 + 16 * (c16 ^ kfold(x))) = R.k[j];
+      }
+    } else {
+      const int a8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = 8 * j + a8;
+        const u32x4_t w = R.k[j];
+        *(bf16x8_t*)(vt + x * 256 + 16 * ((2 * c8) ^ kfold(x))) = fp8x8_to_bf16(u32x2_t{w[0], w[1]});
+        *(bf16x8_t*)(vt + x * 256 + 16 * ((2 * c8 + 1) ^ kfold(x))) = fp8x8_to_bf16(u32x2_t{w[2], w[3]});
+      }
     }
     order_lds();
 #pragma unroll
@@ -605,7 +613,7 @@ void decode_piece_kernel(DecodeArgs a) {
         const __bf16* qrow = a.q + ((int64_t)b * a.Hq + h_base + r) * kD;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          qb[kk] = (r < gcnt) ? *(const bf16x8_t*)(qrow + dmap<DT>(kk, q4)) : zero;
+          qb[kk] = (r < gcnt) ? *(const bf16x8_t*)(qrow + dmap<LAYOUT, DT>(kk, q4)) : zero;
       }
 #pragma unroll
       for (int j = 0; j < kTabCap / 64; ++j)
