@@ -75,6 +75,24 @@ def test_decode_block_sizes(bs):
     _check(st, oracle_cache(st.cache), out, lse, BF16_TOL)
 
 
+@pytest.mark.parametrize("layout,dtype,bs", [("preshuffled", "bf16", 8), ("preshuffled", "bf16", 16),
+                                             ("preshuffled", "bf16", 64), ("preshuffled", "fp8", 16),
+                                             ("preshuffled", "fp8", 32), ("preshuffled", "fp8", 64),
+                                             ("nhd", "fp8", 1), ("nhd", "fp8", 8), ("nhd", "fp8", 64)])
+def test_decode_block_sizes_by_layout(layout, dtype, bs):
+    """Tiles of 32 tokens over blocks of 8 to 64 tokens in every cache kind:
+    the K rows of a tile come from one or several blocks, and lengths end
+    inside a block, inside a tile half and on tile boundaries."""
+    lens = [1, 7, 8, 15, 16, 17, 31, 32, 33, 47, 63, 64, 65, 200, 513]
+    nb = sum(-(-n // bs) for n in lens) + 64
+    st = w.decode_workload(12, len(lens), 16, 2, 128, bs, nb, 1, 600, layout=layout, dtype=dtype,
+                           fixed_lens=lens)
+    w.poison_cache(st.cache, st.block_tables, st.seq_lens)
+    say(f"decode {layout} {dtype} bs={bs} lens={st.seq_lens.tolist()}")
+    out, lse = _run(device_cache(st.cache), st)
+    _check(st, oracle_cache(st.cache), out, lse, BF16_TOL if dtype == "bf16" else FP8_TOL)
+
+
 def test_decode_split_invariance_and_determinism():
     st = w.decode_workload(8, 4, 32, 4, 128, 16, 600, 1500, 2200)
     dc = device_cache(st.cache)
