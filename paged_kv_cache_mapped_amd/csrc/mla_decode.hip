@@ -43,6 +43,7 @@ constexpr int kSlots = 73;                     // 72 16-byte chunks + 1 pad per 
 constexpr int kCopies = (kTileTok * kSlots + 63) / 64;   // 19 copy instructions per tile
 constexpr int kBufBytes = kCopies * 1024;      // 19456
 constexpr int kMWaves = 4;                     // one wave per SIMD (LDS: 8 buffers)
+constexpr int kMlaPlanLds = 2000;              // batches up to this size plan in LDS
 constexpr int kMThreads = 64 * kMWaves;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -63,6 +64,7 @@ struct MlaArgs {
   int32_t max_blocks, num_blocks, bs, bs_log2, H, n_gchunks, batch, max_len;
   int32_t fixed_len, len_min, len_max, target_pieces;
   float qk_mult;              // scale * log2(e)
+  int32_t lds_plan;           // 1: every workgroup plans in LDS (batch <= kMlaPlanLds)
 };
 
 __device__ __forceinline__ int32_t clamp_len16(int32_t L, int32_t cap) {
@@ -146,6 +148,8 @@ __device__ __forceinline__ f32x4_t mfma16k16(s16x4v_t a, s16x4v_t b, f32x4_t c) 
 __global__ __attribute__((amdgpu_flat_work_group_size(kMThreads, kMThreads), amdgpu_waves_per_eu(1, 1)))
 void mla_piece_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves * 2 * kBufBytes];
+  __shared__ int32_t s_cum[kMlaPlanLds + 1];
+  __shared__ int32_t s_wsum[kMWaves];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int q4 = lane >> 4, r = lane & 15;
@@ -164,9 +168,73 @@ void mla_piece_kernel(MlaArgs a) {
     chunk_of[j] = (rr < kTileTok && cc < 72) ? cc : 0;
   }
 
-  const int32_t T = uniform(a.hdr[0]);
-  const int32_t len = uniform(a.hdr[1]);
-  const int32_t NP = uniform(a.hdr[2]);
+  // The plan: prefix sums of the lengths rounded up to 16, the piece length
+  // and the number of pieces.  Small batches plan in every workgroup's LDS
+  // (8 requests per thread, a wave scan, then the wave totals), with no
+  // dependent loads before the first copy; workgroup 0 also leaves the plan
+  // in the workspace for the combine pass.  Larger batches read what
+  // mla_plan_kernel left there.
+  int32_t T, len, NP;
+  if (a.lds_plan) {
+    constexpr int kPer = (kMlaPlanLds + kMThreads - 1) / kMThreads;
+    const int32_t b0 = (int32_t)threadIdx.x * kPer;
+    int32_t v[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      v[i] = b0 + i < a.batch ? (clamp_len16(a.seq_lens[b0 + i], a.max_len) + 15) & ~15 : 0;
+      sum += v[i];
+    }
+    int32_t inc = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int32_t run = inc - sum;
+    T = 0;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) {
+      run += w < wave ? s_wsum[w] : 0;
+      T += s_wsum[w];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (b0 + i < a.batch) s_cum[b0 + i] = run;
+      run += v[i];
+    }
+    if (threadIdx.x == 0) s_cum[a.batch] = T;
+    __syncthreads();
+    T = uniform(T);
+    len = mla_piece_len(a, T);
+    NP = (T + len - 1) / len;
+    if (blockIdx.x == 0) {
+      for (int32_t b = threadIdx.x; b <= a.batch; b += kMThreads) a.cum[b] = s_cum[b];
+      if (threadIdx.x == 0) {
+        a.hdr[0] = T;
+        a.hdr[1] = len;
+        a.hdr[2] = NP;
+      }
+    }
+  } else {
+    T = uniform(a.hdr[0]);
+    len = uniform(a.hdr[1]);
+    NP = uniform(a.hdr[2]);
+  }
+  auto cum_at = [&](int32_t b) -> int32_t { return a.lds_plan ? s_cum[b] : a.cum[b]; };
+  // first request of piece p: the largest b with cum[b] <= p * len (empty
+  // requests share their successor's offset, so the largest one is non-empty)
+  auto first_of = [&](int32_t p) -> int32_t {
+    if (!a.lds_plan) return a.first_seq[p];
+    const int32_t start = p * len;
+    int32_t lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (s_cum[mid] <= start) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
   const int64_t total_waves = (int64_t)gridDim.x * kMWaves;
   const int64_t n_items = (int64_t)NP * a.n_gchunks;
 
@@ -176,8 +244,8 @@ void mla_piece_kernel(MlaArgs a) {
     const int32_t h_base = gc * 16;
     const int gcnt = min(16, a.H - h_base);
     const int32_t pstart = p * len, pend = min(T, pstart + len);
-    for (int32_t b = uniform(a.first_seq[p]); b < a.batch; ++b) {
-      const int32_t cb = uniform(a.cum[b]);
+    for (int32_t b = uniform(first_of(p)); b < a.batch; ++b) {
+      const int32_t cb = uniform(cum_at(b));
       if (cb >= pend) break;
       const int32_t L = uniform(clamp_len16(a.seq_lens[b], a.max_len));
       const int32_t t_begin = max(pstart, cb) - cb;       // multiple of 16
@@ -452,9 +520,13 @@ hipError_t launch_mla_decode(const MlaPlan& p, const void* cache, int32_t num_bl
   a.len_max = p.len_max;
   a.target_pieces = p.target_pieces;
   a.qk_mult = scale * kLog2e;
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  a.lds_plan = batch <= kMlaPlanLds ? 1 : 0;
+  hipError_t e;
+  if (!a.lds_plan) {
+    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(mla_piece_kernel, dim3((unsigned)(p.waves / kMWaves)), dim3(kMThreads), 0, s,
                      a);
   e = hipGetLastError();

@@ -87,6 +87,22 @@ def test_mla_empty_requests():
     _check(st, o, l)
 
 
+@pytest.mark.parametrize("batch", [2000, 2001, 2600])
+def test_mla_large_batches(batch):
+    """Up to 2000 requests the piece kernel plans in its own LDS; above, a
+    planning launch leaves the plan in the workspace.  Both sides of the
+    boundary, short ragged requests (some empty), sampled requests against
+    the oracle."""
+    st = w.mla_decode_workload(86, batch, 16, 16, batch * 7 + 64, 1, 100)
+    st.seq_lens[::97] = 0
+    _poison(st)
+    say(f"mla decode batch {batch}, lengths [0, 100]")
+    out, lse = _run(st)
+    rng = np.random.default_rng(batch)
+    rows = sorted(set(rng.choice(batch, 48, replace=False).tolist()) | {0, 1, batch - 2, batch - 1})
+    _check(st, out, lse, rows)
+
+
 def test_mla_needle():
     """One planted latent row whose score dominates for every head of its
     request: the output is that row's value part (a mis-addressed block would
