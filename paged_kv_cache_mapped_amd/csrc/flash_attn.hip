@@ -552,13 +552,14 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
       // ---- S^T = K Q^T
       f32x16_t s[2];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
+      for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[ks2][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
           s[ks2] = mfma32(*(const bf16x8_t*)(st + 8192 * ks2 + koff[ks]), S.qb[ks], s[ks2]);
-      }
 
       // ---- mask, online softmax on raw scores (row = this lane's query row)
       if constexpr (MASK) {
