@@ -15,7 +15,11 @@
 // wave is an independent worker that owns (piece, KV head, group of up to 16
 // query heads sharing it) and runs one segment per request its piece
 // overlaps, streaming the segment's 32-token tiles.  Per tile the wave:
-//   * loads K rows straight into MFMA A-operand registers (16-byte loads),
+//   * loads K with non-temporal 16-byte loads, every instruction reading
+//     whole 128-byte lines: NHD K as whole token rows (like V), turned into
+//     MFMA A-operand fragments through the wave's LDS slice; preshuffled K
+//     straight into A-operand registers, each subtile taking 8 consecutive
+//     tokens from each 16-token half of the tile,
 //   * computes S^T = K Q^T for its query-head group with v_mfma_f32_16x16x32_bf16
 //     (query heads are the 16 MFMA columns; grouped-query decode is a dense
 //     contraction with G rows),
@@ -25,7 +29,8 @@
 //     rows are staged in the wave's LDS rows with 16-byte coalesced stores and
 //     read back transposed with ds_read_b64_tr_b16; in the preshuffled layout V
 //     is already stored token-minor ([block][head][bs/x][D][x]) and is loaded
-//     straight into registers.
+//     straight into registers, lane rows trading words so that each lane
+//     holds the tokens of its P^T fragment.
 // At the end of a segment the wave writes either the final output (a request
 // inside one piece) or an fp32 partial (o, lse) that a second kernel merges
 // with LSE weights.  The partial of piece p of request b goes to row p + b:
