@@ -14,9 +14,9 @@
 //   and an LSE merge, (3) a final merge.  Each chunk yields an output and an
 //   LSE that records its softmax denominator.
 //
-// Tile core.  A workgroup of 8 waves owns two blocks of 128 query rows that
-// read the same keys -- two query heads of one KV head, or two consecutive
-// query tiles of one head -- 32 rows per wave, and walks the key range in
+// Tile core.  A workgroup of 8 waves owns 256 query rows that read the same
+// keys -- P = gcd(G, 8) query heads of one KV head over 256 / P consecutive
+// tokens, each wave one head over 32 tokens -- and walks the key range in
 // tiles of 64 keys staged in LDS (double buffered: the next tile is moved from
 // global memory straight into the other LDS buffer by global_load_lds_dwordx4
 // while the current one is consumed, with no staging registers).  Each tile
@@ -53,7 +53,8 @@ namespace pkv {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kBM = 128;                   // query rows per row block
+constexpr int kBM = 128;                   // query tile of the work-size heuristics
+constexpr int kWGRows = 256;               // query rows (token, head) per workgroup
 constexpr int kWaves = 8;                  // two row blocks of 4 waves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;                    // keys per tile
@@ -78,10 +79,11 @@ struct AttnArgs {
   float* part_lse;          // [n_parts][rows][Hq]
   int32_t max_blocks, num_blocks, bs, bs_log2;
   int32_t Hq, Hkv, G, num_seqs, n_parts, chunk_tokens, rows;
-  int32_t pairs;            // 1: a work item is two query heads of one KV head over the
-                            // same 128 rows; 0: two consecutive 128-row tiles of one head
-  int32_t Gs;               // lanes per KV head: G / 2 (pairs) or G
-  int32_t n_qitems;         // query items per lane: 128-row tiles (pairs) or tile pairs
+  int32_t P;                // query heads per workgroup (gcd(G, 8)): wave w takes head
+                            // w % P of the lane's P heads, tokens 32 (w / P) .. + 31
+  int32_t TW;               // tokens per workgroup: kWGRows / P
+  int32_t Gs;               // lanes per KV head: G / P
+  int32_t n_qitems;         // query items per lane: TW-token slices of the sequence
   int64_t items;            // lanes (work items = lanes x query items)
   int64_t grid_pad;         // launched workgroups (multiple of 8)
   int32_t qt_major;         // work order inside an XCD's share of lanes
@@ -101,14 +103,16 @@ struct AttnArgs {
 };
 
 // Work order.  A work item is (lane, query item), lanes being the
-// (sequence[, part], KV head, query-head pair or query head) combinations in
-// that order.  A workgroup of 8 waves runs two 128-row blocks that share every
-// K/V tile it copies into LDS: two query heads of one KV head over the same
-// rows when the group size is even, else two consecutive query tiles of one
-// head.
+// (sequence[, part], KV head, group of P query heads) combinations in that
+// order.  A workgroup of 8 waves runs 256 query rows that share every K/V tile
+// it copies into LDS: P query heads of one KV head over TW = 256 / P
+// consecutive tokens, each wave one head over 32 tokens (P = gcd(G, 8): eight
+// heads over 32 tokens for groups of 8 or 16, one head over 256 tokens for an
+// odd group).  Short requests then fill their rows, and a workgroup's causal
+// diagonal is TW tokens long.
 // Launched workgroup L runs on XCD L % 8, and the hardware hands workgroups
 // out in launch order as CUs free up.  Lanes are dealt to the XCDs in chunks
-// of lchunk consecutive lanes (half the query-head pairs of one KV head): the
+// of lchunk consecutive lanes (half the head groups of one KV head): the
 // heads of a chunk share its K/V tiles in that XCD's L2, and the lanes of one
 // request -- 2 * H_kv chunks -- are spread over the XCDs, so a request that
 // is much longer than the others (a heavy-tailed batch) is worked on by the
@@ -166,27 +170,21 @@ static unsigned persistent_grid(int64_t grid_pad, hipStream_t stream) {
   return (unsigned)(grid_pad < slots ? grid_pad : slots);
 }
 
-// This wave's row block of work item (KV head hkv, lane-in-group gsel, query
-// item qi): waves 0-3 take block 0, waves 4-7 block 1.  q0 is the block's
-// first row; q0_lo / q0_hi the first rows of the workgroup's first / last
-// block (they bound the keys the workgroup needs under a causal mask).
+// This wave's rows of work item (KV head hkv, head group gsel, query item qi):
+// query head h over tokens q0w .. q0w + 31; the workgroup's tokens are
+// [q0_lo, q_end) (they bound the keys it needs under a causal mask).
 struct RowBlock {
-  int32_t h, q0, q0_lo, q0_hi;
+  int32_t h, q0w, q0_lo, q_end;
 };
 template <class Args>
 __device__ __forceinline__ RowBlock row_block(const Args& a, int32_t hkv, int32_t gsel,
                                               int32_t qi) {
-  const int rb = wave_id() >> 2;
+  const int w = wave_id();
   RowBlock r;
-  if (a.pairs) {
-    r.h = hkv * a.G + 2 * gsel + rb;
-    r.q0 = r.q0_lo = r.q0_hi = qi * kBM;
-  } else {
-    r.h = hkv * a.G + gsel;
-    r.q0_lo = 2 * qi * kBM;
-    r.q0_hi = r.q0_lo + kBM;
-    r.q0 = r.q0_lo + rb * kBM;
-  }
+  r.h = hkv * a.G + gsel * a.P + (w & (a.P - 1));
+  r.q0_lo = qi * a.TW;
+  r.q_end = r.q0_lo + a.TW;
+  r.q0w = r.q0_lo + 32 * (w / a.P);
   return r;
 }
 
@@ -467,13 +465,13 @@ struct RowState {
   float m_run, l_run;
 };
 
-// Load Q (rows q0.. of a sequence whose row 0 is global row qbase) and clear
-// the running state.
-__device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t qbase, int32_t q0,
+// Load Q (this wave's rows q0w .. q0w + 31 of a sequence whose row 0 is
+// global row qbase) and clear the running state.
+__device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t qbase, int32_t q0w,
                                           int32_t qn, RowState& S) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int32_t row = q0 + 32 * (wave & 3) + r;
+  const int32_t row = q0w + r;
   // Q^T as the B operand: lane holds q[row][16*ks + 8*hh .. +8], ks = 0..7
   const bf16x8_t zero = {};
   const __bf16* qp = a.q + ((qbase + row) * a.Hq + h) * kD + 8 * hh;
@@ -488,8 +486,8 @@ __device__ __forceinline__ void init_rows(const AttnArgs& a, int32_t h, int64_t 
 }
 
 // The tile loop folding keys [k_begin, kend) (n_tiles tiles of kBN) into the
-// running state of this wave's rows (block starting at q0; the workgroup's
-// first block starts at q0_lo).  CAUSAL: key j is visible to row i iff j <= i
+// running state of this wave's rows (tokens q0w .. q0w + 31; the workgroup's
+// first token is q0_lo).  CAUSAL: key j is visible to row i iff j <= i
 // (keys and rows indexed within the sequence).  On entry the first tile is in
 // LDS buffer SB, published by a barrier, and blk_next holds the table entry
 // of the second one (paged keys).  Tile t is in buffer (t + SB) & 1; each step
@@ -501,14 +499,13 @@ struct NoHooks {
 };
 template <bool PAGED, bool CAUSAL, int SB, class Hooks, class Args, int KIND = kCtxNhdBf16>
 __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const KeySrc& src,
-                                         int32_t q0, int32_t q0_lo, int32_t k_begin, int32_t kend,
+                                         int32_t q0w, int32_t q0_lo, int32_t k_begin, int32_t kend,
                                          int32_t n_tiles, int32_t blk_next, RowState& S,
                                          const Hooks& hooks) {
   const int lane = lane_here();
-  const int wave = wave_id();
   const int r = lane & 31, hh = lane >> 5;      // MFMA column (query row) / k-half
   const int g16 = lane >> 4, l16 = lane & 15;   // 16-lane group for transposed reads
-  const int32_t row = q0 + 32 * (wave & 3) + r; // this lane's query row (in sequence)
+  const int32_t row = q0w + r;                  // this lane's query row (in sequence)
   const float qk = KIND == kCtxNhdBf16 ? a.qk_mult : a.ctx_qk_mult;
   const float vexp = a.ctx_vexp, linv = a.ctx_linv;
 
@@ -547,7 +544,7 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
     // A diagonal tile whose first key lies past every row of this wave
     // contributes nothing to it: the wave only takes part in the copy and the
     // barrier.
-    const bool skip = MASK && CAUSAL && k0 > q0 + 32 * (wave & 3) + 31;
+    const bool skip = MASK && CAUSAL && k0 > q0w + 31;
     if (!skip) {
       // ---- S^T = K Q^T
       f32x16_t s[2];
@@ -670,20 +667,17 @@ __device__ __forceinline__ void key_loop(const Args& a, uint8_t* smem, const Key
 
 
 // Fold keys [k_begin, k_end) of one source into the running state of this
-// wave's rows (block starting at q0; the workgroup's blocks start at q0_lo and
-// q0_hi): copy the first tile, then the tile loop.  The LDS double buffer is
+// wave's rows (tokens q0w .. q0w + 31; the workgroup's tokens are [q0_lo,
+// q_end)): copy the first tile, then the tile loop.  The LDS double buffer is
 // filled and drained inside, so phases with different sources can follow
 // each other.
 template <bool PAGED, bool CAUSAL, bool FIRST = false, int KIND = kCtxNhdBf16>
 __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const KeySrc& src,
-                                         int32_t q0, int32_t q0_lo, int32_t q0_hi, int32_t qn,
+                                         int32_t q0w, int32_t q0_lo, int32_t q_end, int32_t qn,
                                          int32_t k_begin, int32_t k_end, RowState& S) {
-  // key range actually needed by this block
+  // key range actually needed by the workgroup
   int32_t kend = k_end;
-  if constexpr (CAUSAL) {
-    const int32_t last_row = min(q0_hi + kBM, qn) - 1;
-    kend = min(kend, last_row + 1);
-  }
+  if constexpr (CAUSAL) kend = min(kend, min(q_end, qn));
   if (kend <= k_begin) return;               // uniform over the workgroup
   const int32_t n_tiles = (kend - k_begin + kBN - 1) / kBN;
 
@@ -707,18 +701,18 @@ __device__ __forceinline__ void run_keys(const AttnArgs& a, uint8_t* smem, const
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(S.qb[ks]));
   __syncthreads();
-  key_loop<PAGED, CAUSAL, 0, NoHooks, AttnArgs, KIND>(a, smem, src, q0, q0_lo, k_begin, kend,
+  key_loop<PAGED, CAUSAL, 0, NoHooks, AttnArgs, KIND>(a, smem, src, q0w, q0_lo, k_begin, kend,
                                                      n_tiles, blk_next, S, NoHooks{});
 }
 
-// Write the rows of this block: bf16 output + lse, or an fp32 partial
-// (normalised o and its lse) of part `part`.
+// Write this wave's rows: bf16 output + lse, or an fp32 partial (normalised
+// o and its lse) of part `part`.
 template <bool PARTIAL>
 __device__ __forceinline__ void finish_rows(const AttnArgs& a, int32_t h, int64_t qbase,
-                                            int32_t q0, int32_t qn, int32_t part, RowState& S) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+                                            int32_t q0w, int32_t qn, int32_t part, RowState& S) {
+  const int lane = threadIdx.x & 63;
   const int r = lane & 31, hh = lane >> 5;
-  const int32_t row = q0 + 32 * (wave & 3) + r;
+  const int32_t row = q0w + r;
   const float l_run = xor32_sum(S.l_run);
   if (row >= qn) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -828,12 +822,12 @@ __device__ __forceinline__ StreamItem next_item(int32_t& r) {
     if (rb.q0_lo >= qn) continue;
     it.valid = 1;
     it.h = uniform(rb.h);
-    it.q0w = uniform(rb.q0 + 32 * (wave_id() & 3));
+    it.q0w = uniform(rb.q0w);
     it.q0_lo = uniform(rb.q0_lo);
     it.qn = uniform(qn);
     it.s0 = uniform(s0);
     it.hkv = uniform(hkv);
-    it.kend = uniform(CAUSAL ? min(rb.q0_hi + kBM, qn) : qn);
+    it.kend = uniform(CAUSAL ? min(rb.q_end, qn) : qn);
     it.n_tiles = uniform((it.kend + kBN - 1) / kBN);
     ++r;
     return it;
@@ -976,13 +970,12 @@ void prefill_stream_kernel(AttnArgs) {
       const ArgsPtr A = args_here();
       const NextItem<CAUSAL> hooks = {A, smem, &r};
       const KeySrc src = contiguous_keys(*A, cur.s0, cur.hkv);
-      const int32_t q0 = cur.q0w - 32 * (wave_id() & 3);
       if (sb == 0)
-        key_loop<false, CAUSAL, 0>(*A, smem, src, q0, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0, S,
-                                   hooks);
+        key_loop<false, CAUSAL, 0>(*A, smem, src, cur.q0w, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0,
+                                   S, hooks);
       else
-        key_loop<false, CAUSAL, 1>(*A, smem, src, q0, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0, S,
-                                   hooks);
+        key_loop<false, CAUSAL, 1>(*A, smem, src, cur.q0w, cur.q0_lo, 0, cur.kend, cur.n_tiles, 0,
+                                   S, hooks);
     }
     sb = (sb + cur.n_tiles) & 1;
     // The last tile's barrier has passed: the next item's Q and first tile are in LDS.
@@ -998,7 +991,7 @@ void prefill_stream_kernel(AttnArgs) {
   }
 }
 
-// Split extend.  Lanes: (seq, part, kv head, query-head pair or query head).  Part 0: the new
+// Split extend.  Lanes: (seq, part, kv head, group of P query heads).  Part 0: the new
 // tokens among themselves (causal).  Part
 // p >= 1: the new tokens against context chunk p-1 = cached tokens
 // [(p-1)*chunk, p*chunk), read through the block table.  Every part writes an
@@ -1027,20 +1020,20 @@ __device__ __forceinline__ void split_item(const AttnArgs& a, uint8_t* smem, int
   if (rb.q0_lo >= qn) return;                            // uniform over the workgroup
   RowState S;
   if (part == 0) {
-    init_rows(a, rb.h, s0, rb.q0, qn, S);
-    run_keys<false, true, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
+    init_rows(a, rb.h, s0, rb.q0w, qn, S);
+    run_keys<false, true, true>(a, smem, contiguous_keys(a, s0, hkv), rb.q0w, rb.q0_lo, rb.q_end,
                                 qn, 0, qn, S);
   } else {
     const int32_t C = context_len(a, seq);
     const int32_t kb = (part - 1) * a.chunk_tokens;
     if (kb >= C) return;
-    init_rows(a, rb.h, s0, rb.q0, qn, S);
-    run_keys<true, false, true, KIND>(a, smem, paged_keys(a, seq, hkv), rb.q0, rb.q0_lo, rb.q0_hi,
+    init_rows(a, rb.h, s0, rb.q0w, qn, S);
+    run_keys<true, false, true, KIND>(a, smem, paged_keys(a, seq, hkv), rb.q0w, rb.q0_lo, rb.q_end,
                                       qn, kb, min(C, kb + a.chunk_tokens), S);
   }
   // partial rows: the request's own rows, or (hybrid, slot >= 0) its compact rows
   const int64_t pbase = slot < 0 ? s0 : uniform(a.plan[kPlanHead + a.max_split + slot]);
-  finish_rows<true>(a, rb.h, pbase, rb.q0, qn, part, S);
+  finish_rows<true>(a, rb.h, pbase, rb.q0w, qn, part, S);
 }
 
 template <int KIND>
@@ -1060,8 +1053,8 @@ void extend_kernel(AttnArgs a) {
 }
 
 // Fused extend, used when the batch has enough query tiles to fill the GPU
-// without splitting along the context.  Logical order: (seq, kv head, query
-// head pair or head, query item descending).  One workgroup runs the cached
+// without splitting along the context.  Logical order: (seq, kv head, head
+// group, query item descending).  One workgroup runs the cached
 // context of its rows and then the new tokens, carrying one running softmax
 // state: the LSE merge of the context into the running output is done in
 // registers (rescaling by the exponential of the max difference), so no
@@ -1082,10 +1075,10 @@ __device__ __forceinline__ void fused_item(const AttnArgs& a, uint8_t* smem, int
   StreamItem it = {};
   it.valid = 1;
   it.h = rb.h;
-  it.q0w = rb.q0 + 32 * (wave_id() & 3);
+  it.q0w = rb.q0w;
   it.qn = qn;
   it.s0 = s0;
-  const int32_t kend = min(rb.q0_hi + kBM, qn);          // new tokens, causal
+  const int32_t kend = min(rb.q_end, qn);                // new tokens, causal
   const KeySrc ctx = paged_keys(a, seq, hkv);
   const KeySrc fresh = contiguous_keys(a, s0, hkv);
   dma_q(a, smem, it);
@@ -1109,12 +1102,12 @@ __device__ __forceinline__ void fused_item(const AttnArgs& a, uint8_t* smem, int
   clear_rows(S);
   if (C > 0) {
     const int32_t nt = (C + kBN - 1) / kBN;
-    key_loop<true, false, 0, NoHooks, AttnArgs, KIND>(a, smem, ctx, rb.q0, rb.q0_lo, 0, C, nt,
+    key_loop<true, false, 0, NoHooks, AttnArgs, KIND>(a, smem, ctx, rb.q0w, rb.q0_lo, 0, C, nt,
                                                       blk1, S, NoHooks{});
-    run_keys<false, true>(a, smem, fresh, rb.q0, rb.q0_lo, rb.q0_hi, qn, 0, qn, S);
+    run_keys<false, true>(a, smem, fresh, rb.q0w, rb.q0_lo, rb.q_end, qn, 0, qn, S);
   } else {
     const int32_t nt_new = (kend + kBN - 1) / kBN;
-    key_loop<false, true, 0>(a, smem, fresh, rb.q0, rb.q0_lo, 0, kend, nt_new, 0, S, NoHooks{});
+    key_loop<false, true, 0>(a, smem, fresh, rb.q0w, rb.q0_lo, 0, kend, nt_new, 0, S, NoHooks{});
   }
   store_rows(a, smem, rb.h, s0, it.q0w, qn, S);
 }
@@ -1133,8 +1126,8 @@ void extend_fused_kernel(AttnArgs a) {
   fused_item<KIND>(a, smem, seq, hkv, gsel, w.qi);
 }
 
-// Hybrid extend over the plan's work list: lanes are the (KV head, pair or
-// head) combinations, query items the list positions (heaviest first, the
+// Hybrid extend over the plan's work list: lanes are the (KV head, head
+// group) combinations, query items the list positions (heaviest first, the
 // positions past the list's length empty and launched last).  An entry runs
 // fused (its request's context and new tokens, one running state) or as one
 // part of a split request (partials in compact rows, merged afterwards).
@@ -1214,9 +1207,9 @@ __device__ __forceinline__ int32_t block_scan_1024(int32_t v, int32_t* s_tmp, in
 }
 
 // Plan of the hybrid extend (one workgroup, one request per thread).  A fused
-// work item of request b (n_b new tokens, C_b cached) with rows [i R, (i+1) R)
+// work item of request b (n_b new tokens, C_b cached) with tokens [i R, (i+1) R)
 // walks ceil(C_b/64) context tiles and ceil(min((i+1) R, n_b)/64) new-token
-// tiles (R = 128 rows for head pairs, 256 for two row tiles of one head); its
+// tiles (R = TW tokens per workgroup); its
 // longest item walks walk_b = ceil(C_b/64) + ceil(n_b/64).  The batch's work,
 // summed over every item, spread over the resident workgroups gives the mean
 // load D.  A request with walk_b > D / 2 holds workgroups for a large part of
@@ -1236,14 +1229,15 @@ __global__ __launch_bounds__(1024) void extend_plan_kernel(AttnArgs a) {
   __shared__ int32_t s_cnt[kHybridMaxSeqs];
   __shared__ int32_t s_slot[kHybridMaxSeqs];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int32_t R = a.pairs ? kBM : 2 * kBM;
+  const int32_t R = a.TW;
   int32_t* plan = (int32_t*)a.plan;
   const bool mine = t < a.num_seqs;
   const int32_t n = mine ? a.cu[t + 1] - a.cu[t] : 0;
   const int32_t C = mine ? context_len(a, t) : 0;
   const int32_t k = (n + R - 1) / R;                      // query items per lane
   const int32_t ct = (C + kBN - 1) / kBN, nt = (n + kBN - 1) / kBN;
-  int64_t w = n > 0 ? (int64_t)a.Hkv * a.Gs * ((int64_t)k * ct + (R / kBN) * (int64_t)(k - 1) * k / 2 + nt)
+  int64_t w = n > 0 ? (int64_t)a.Hkv * a.Gs *
+                          ((int64_t)k * ct + (int64_t)R * (k - 1) * k / 2 / kBN + nt)
                     : 0;
   for (int off = 32; off > 0; off >>= 1) w += __shfl_xor(w, off);
   if (lane == 0) s_w[wave] = w;
@@ -1367,12 +1361,22 @@ int32_t log2i(int32_t v) {
 
 }  // namespace
 
-// Row blocks of a work item: two query heads of one KV head when the group
-// size is even, else two consecutive query tiles of one head.
-static void set_pairing(AttnArgs& a, int32_t n_qtiles) {
-  a.pairs = (a.G % 2 == 0) ? 1 : 0;
-  a.Gs = a.pairs ? a.G / 2 : a.G;
-  a.n_qitems = a.pairs ? n_qtiles : (n_qtiles + 1) / 2;
+// Query heads per workgroup: the largest power of two up to 8 dividing the
+// group size G.
+static int32_t heads_per_wg(int32_t G) {
+  int32_t P = 1;
+  while (P < 8 && G % (2 * P) == 0) P *= 2;
+  return P;
+}
+
+// Rows of a work item: P query heads of one KV head over TW = 256 / P tokens;
+// lanes per KV head and query items per lane for sequences of up to
+// max_tokens tokens.
+static void set_packing(AttnArgs& a, int32_t max_tokens) {
+  a.P = heads_per_wg(a.G);
+  a.TW = kWGRows / a.P;
+  a.Gs = a.G / a.P;
+  a.n_qitems = (max_tokens + a.TW - 1) / a.TW;
   a.lchunk = a.Gs >= 2 ? a.Gs / 2 : 1;
 }
 
@@ -1391,8 +1395,7 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const int
   a.Hkv = num_kv_heads;
   a.G = num_q_heads / num_kv_heads;
   a.num_seqs = num_seqs;
-  const int32_t n_qtiles = (max_seqlen + kBM - 1) / kBM;
-  set_pairing(a, n_qtiles);
+  set_packing(a, max_seqlen);
   a.n_parts = 1;
   a.qk_mult = scale * kLog2e;
   a.items = (int64_t)num_seqs * num_kv_heads * a.Gs;     // lanes
@@ -1446,7 +1449,7 @@ ExtendPlan plan_extend(const kv_cache_t& c, int32_t num_seqs, int32_t total_new,
     // list length bound: a fused request has at most n/R + 1 query items, a
     // split one n_parts times that, and the split requests' rows are at most
     // cap_rows
-    const int64_t R = (num_q_heads / c.num_kv_heads) % 2 == 0 ? kBM : 2 * kBM;
+    const int64_t R = kWGRows / heads_per_wg(num_q_heads / c.num_kv_heads);
     const int64_t cap_list = (total_new + R - 1) / R + num_seqs +
                              (int64_t)p.n_parts * ((p.cap_rows + R - 1) / R + p.max_split);
     p.list_cap = (int32_t)(cap_list < (1 << 24) ? cap_list : 0);
@@ -1504,7 +1507,7 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
   a.G = num_q_heads / c.num_kv_heads;
   a.num_seqs = num_seqs;
   const int32_t n_qtiles = (max_q_len + kBM - 1) / kBM;
-  set_pairing(a, n_qtiles);
+  set_packing(a, max_q_len);
   a.n_parts = p.n_parts;
   a.chunk_tokens = p.chunk_tokens;
   a.rows = total_new;
@@ -1520,7 +1523,7 @@ hipError_t launch_extend(const kv_cache_t& c, const ExtendPlan& p, const void* q
     a.max_split = p.max_split;
     a.list_cap = p.list_cap;
     a.plan_slots = device_cu_count(s);
-    a.items = (int64_t)a.Hkv * a.Gs;                     // lanes: (KV head, pair or head)
+    a.items = (int64_t)a.Hkv * a.Gs;                     // lanes: (KV head, head group)
     a.n_qitems = p.list_cap;                             // list positions
     a.qt_major = 1;
     // an XCD's share of the lanes: an eighth of them, within one KV head or
