@@ -219,12 +219,14 @@ def test_extend_workspace_by_mode():
     # context of 7 chunks -> hybrid: the plan (4 header words, per split slot
     # a request and a first compact row), the work list (16 bytes per entry:
     # at most T/R + E query items of fused requests and n_parts x (cap_rows/R
-    # + slots) of split ones, R = 128 rows for head pairs) and the partials of
-    # at most 64 MiB of compact rows
+    # + slots) of split ones, R = 256 / P tokens per workgroup, P = 8 query
+    # heads for a group of 8) and the partials of at most 64 MiB of compact
+    # rows
     slots = min(E, 16)
     cap_rows = min(T, (64 << 20) // (parts * Hq * 129 * 4))
     crow = parts * cap_rows * Hq
-    list_cap = -(-T // 128) + E + parts * (-(-cap_rows // 128) + slots)
+    R = 256 // 8
+    list_cap = -(-T // R) + E + parts * (-(-cap_rows // R) + slots)
     assert ws(pk.KV_EXTEND_AUTO) == (a256(4 * (4 + 2 * slots)) + a256(16 * list_cap) +
                                      a256(crow * 128 * 4) + a256(crow * 4))
     # a context within one chunk leaves nothing to split: plain fused
