@@ -115,10 +115,10 @@ def test_extend_split_long_context_full_size_sampled():
 
 @pytest.mark.parametrize("mode", ["auto", "fused", "split"])
 def test_extend_odd_query_group(mode):
-    """24 query heads : 8 KV heads (group of 3): work items pair consecutive
-    128-row query tiles of one head instead of two heads.  5600 new tokens
-    give 24 * 44 = 1056 query tiles, enough for the automatic plan to fuse on
-    256 compute units.  Every row against the oracle."""
+    """24 query heads : 8 KV heads (group of 3): a work item is one query head
+    over 256 tokens (an odd group has no power-of-two head split).  5600 new
+    tokens give 24 * 44 = 1056 query tiles of 128, enough for the automatic
+    plan to fuse on 256 compute units.  Every row against the oracle."""
     mb = w.mixed_batch(45, 24, 8, 128, 16, 700, [], [1000, 77], [2900, 2700], [])
     w.poison_cache(mb.cache, mb.ext_tables, mb.ext_ctx)
     say(f"extend 24:8 mode={mode} new [2900, 2700] ctx [1000, 77]")
