@@ -1228,6 +1228,8 @@ __global__ __launch_bounds__(1024) void extend_plan_kernel(AttnArgs a) {
   __shared__ uint32_t s_key[kHybridMaxSeqs];
   __shared__ int32_t s_cnt[kHybridMaxSeqs];
   __shared__ int32_t s_slot[kHybridMaxSeqs];
+  __shared__ int32_t s_off[kHybridMaxSeqs + 1];   // first list entry of sorted position q
+  __shared__ int32_t s_req[kHybridMaxSeqs];       // request at sorted position q
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t R = a.TW;
   int32_t* plan = (int32_t*)a.plan;
@@ -1291,28 +1293,40 @@ __global__ __launch_bounds__(1024) void extend_plan_kernel(AttnArgs a) {
       __syncthreads();
     }
   }
-  // thread t writes the entries of the request at sorted position t
+  // offsets of the sorted requests' entries, then every thread writes entries
+  // j = t, t + 1024, ...: entry j belongs to the last sorted position whose
+  // first entry is <= j (positions without entries share their successor's
+  // offset)
   const uint32_t key = t < N ? s_key[t] : 0xFFFFFFFFu;
   const int32_t b = key != 0xFFFFFFFFu ? (int32_t)(key & 0x3FFu) : -1;
   const int32_t bcnt = b >= 0 ? s_cnt[b] : 0;
   int32_t total;
   const int32_t off = block_scan_1024(bcnt, s_tmp, &total);
   const int32_t E = total < a.list_cap ? total : a.list_cap;
-  if (bcnt > 0) {
-    ListEntry* list = (ListEntry*)a.list;
-    const int32_t bn = a.cu[b + 1] - a.cu[b];
-    const int32_t bk = (bn + R - 1) / R;
-    const int32_t bslot = s_slot[b];
-    const int32_t bparts = bcnt / bk;
-    for (int32_t i = 0; i < bcnt && off + i < E; ++i) {
-      ListEntry e;
-      e.seq = b;
-      e.slot = bslot;
-      e.qi = bk - 1 - i % bk;                             // later query items first
-      const int32_t pi = i / bk;                          // context chunks first, new tokens last
-      e.part = bslot < 0 ? 0 : (pi + 1 < bparts ? pi + 1 : 0);
-      list[off + i] = e;
+  if (t < N) {
+    s_off[t] = off;
+    s_req[t] = b;
+  }
+  __syncthreads();
+  ListEntry* list = (ListEntry*)a.list;
+  for (int32_t j = t; j < E; j += 1024) {
+    int32_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
     }
+    const int32_t rb = s_req[lo], i = j - s_off[lo];
+    const int32_t bn = a.cu[rb + 1] - a.cu[rb];
+    const int32_t bk = (bn + R - 1) / R;
+    const int32_t bslot = s_slot[rb];
+    const int32_t bparts = s_cnt[rb] / bk;
+    ListEntry e;
+    e.seq = rb;
+    e.slot = bslot;
+    e.qi = bk - 1 - i % bk;                               // later query items first
+    const int32_t pi = i / bk;                            // context chunks first, new tokens last
+    e.part = bslot < 0 ? 0 : (pi + 1 < bparts ? pi + 1 : 0);
+    list[j] = e;
   }
   if (t == 0) {
     plan[0] = n_split;
