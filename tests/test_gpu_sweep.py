@@ -16,15 +16,26 @@ from .gpu_util import (BF16_TOL, FP8_TOL, LSE_TOL, bf16_to_f64, dev, device_cach
 pytestmark = pytest.mark.gpu
 
 N_CASES = 60
+HEADS = [(8, 8), (8, 1), (16, 2), (12, 4), (6, 2), (64, 4), (64, 8), (5, 1), (32, 4)]
+# group sizes 2, 4, 6, 12 and 24: a workgroup takes 2, 4, 2, 4 and 8 query
+# heads (gcd(G, 8)) over 128, 64, 128, 64 and 32 tokens
+MORE_GROUPS = [(8, 4), (16, 4), (12, 2), (24, 2), (48, 2)]
 
 
 def test_random_shapes_against_oracle():
+    _sweep(2024, N_CASES, HEADS)
+
+
+def test_random_shapes_more_head_groups():
+    _sweep(2025, 30, MORE_GROUPS)
+
+
+def _sweep(seed0, n_cases, HEADS):
     t = torch()
-    rng = np.random.default_rng(2024)
-    HEADS = [(8, 8), (8, 1), (16, 2), (12, 4), (6, 2), (64, 4), (64, 8), (5, 1), (32, 4)]
+    rng = np.random.default_rng(seed0)
     worst = {}
     fails = []
-    for n in range(1, N_CASES + 1):
+    for n in range(1, n_cases + 1):
         kind = rng.choice(['prefill', 'extend', 'decode'])
         Hq, Hkv = HEADS[rng.integers(len(HEADS))]
         seed = int(rng.integers(1 << 30))
