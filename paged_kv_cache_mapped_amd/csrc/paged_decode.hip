@@ -410,14 +410,13 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t cap) {
 }
 
 // Piece length from the padded stream length T (same rule in both planners).
-// Pieces are 1/8 longer than an even share per wave: about one wave in nine
+// Pieces are 1/4 longer than an even share per wave: about one wave in five
 // then has no piece, but HBM stays saturated and the kernel has fewer
-// per-piece start-ups and partials to write and merge (measured 2-3.5%
-// faster on the decode layer, the fp8 decode and the mixed batch's decode).
+// per-piece start-ups and partials to write and merge.
 __device__ __forceinline__ int32_t piece_len(const DecodeArgs& a, int32_t T) {
   if (a.fixed_len > 0) return a.fixed_len;
   int32_t len = (T + a.target_pieces - 1) / a.target_pieces;
-  len += len / 8;
+  len += len / 4;
   len = (len + 31) & ~31;
   return len < a.len_min ? a.len_min : (len > a.len_max ? a.len_max : len);
 }
