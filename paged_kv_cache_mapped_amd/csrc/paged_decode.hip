@@ -111,18 +111,24 @@ __device__ __forceinline__ int dmap(int kk, int q4) {
 // are 4 q4 .. 4 q4 + 3); the score of that token is probability k-slot
 // 4 s + i of the lane's P^T fragment.  Default: k-slots 8 q4 .. 8 q4 + 7 are
 // tokens 8 q4 .. 8 q4 + 7 of the tile.  The preshuffled K cache stores the
-// tokens of a block consecutively for each 16-byte dim chunk, so there each
-// subtile takes 8 consecutive tokens from each 16-token half of the tile --
-// every K load instruction then reads whole 128-byte lines -- and lane
-// quarter q4 ends up with tokens of half q4 / 2 only.
+// tokens of a block consecutively for each 16-byte dim chunk.  With bf16
+// (8-token V x-groups) each subtile takes one whole 16-token block -- every
+// K load instruction reads 256-byte runs -- and lane quarter q4 gets tokens
+// 4 q4 .. + 3 of both blocks.  With fp8 (16-token V x-groups) each subtile
+// takes 8 consecutive tokens from each 16-token half of the tile (128-byte
+// runs), so that lane quarter q4 ends up with tokens of half q4 / 2 only; in
+// both cases one swap between lane rows q4 and q4 ^ 1 builds the V^T
+// fragments (see consume_tile).
 template <int LAYOUT, int DT>
 __device__ __forceinline__ int k_row_token(int s, int rr) {
-  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (rr >> 3) + 8 * s + (rr & 7);
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_BF16) return 16 * s + rr;
+  else if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (rr >> 3) + 8 * s + (rr & 7);
   else return 8 * (rr >> 2) + 4 * s + (rr & 3);
 }
 template <int LAYOUT, int DT>
 __device__ __forceinline__ int score_token(int q4, int s, int i) {
-  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (q4 >> 1) + 8 * s + 4 * (q4 & 1) + i;
+  if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED && DT == KV_DTYPE_BF16) return 16 * s + 4 * q4 + i;
+  else if constexpr (LAYOUT == KV_LAYOUT_PRESHUFFLED) return 16 * (q4 >> 1) + 8 * s + 4 * (q4 & 1) + i;
   else return 8 * q4 + 4 * s + i;
 }
 
@@ -213,7 +219,10 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, const int32_t* s
       R.v[j] = stream_load((const u32x4_t*)(a.vc + (base + 16 * (2 * j + (q4 & 1)) + r) * 16));
   } else {
     constexpr int X = 8;                                        // bf16
-    const int32_t tb = min(t0 + 8 * q4, (t_end - 1) & ~7);   // 8 tokens, aligned to 8
+    // 8-token group ((q4 & 1) << 1) | (q4 >> 1): lane rows q4 and q4 ^ 1 hold
+    // groups g and g + 2 (the same 4-token quarters of both 16-token blocks)
+    const int grp = ((q4 & 1) << 1) | (q4 >> 1);
+    const int32_t tb = min(t0 + 8 * grp, (t_end - 1) & ~7);   // 8 tokens, aligned to 8
     const int32_t blk = s_tab[(tb >> a.bs_log2) - ib0];
     const int32_t off = tb & (a.bs - 1);
     const int64_t base = (((int64_t)blk * a.Hkv + hkv) * (a.bs / X) + off / X) * kD;
@@ -309,11 +318,13 @@ __device__ __forceinline__ void consume_tile(const DecodeArgs& a, const TileRaw&
     }
   } else {
     if constexpr (DT == KV_DTYPE_BF16) {
-      // Load n of lane (q4, r) holds tokens 8 q4 .. 8 q4 + 7 of dim 16 n + r,
-      // two per word.  The lane's P^T k-slots are tokens 0-3 (even q4) or
-      // 4-7 (odd q4) of 8-token groups q4 & ~1 and q4 | 1: swapping (w0, w1)
-      // of the odd rows of 16 lanes with (w2, w3) of the even rows leaves
-      // exactly those, in k-slot order.
+      // Load n of lane (q4, r) holds the 8 tokens of group g = 2 (q4 & 1) +
+      // q4 / 2 (tokens 8 g .. 8 g + 7) of dim 16 n + r, two per word.  The
+      // lane's P^T k-slots are tokens 4 q4 .. + 3 and 16 + 4 q4 .. + 3: the
+      // first or second halves of groups q4 / 2 and q4 / 2 + 2, which lane rows
+      // q4 and q4 ^ 1 hold between them.  Swapping (w0, w1) of the odd rows of
+      // 16 lanes with (w2, w3) of the even rows leaves exactly those, in
+      // k-slot order.
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         uint32_t w0 = R.v[n][0], w1 = R.v[n][1], w2 = R.v[n][2], w3 = R.v[n][3];
