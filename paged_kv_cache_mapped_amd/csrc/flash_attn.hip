@@ -55,7 +55,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBM = 128;                   // query tile of the work-size heuristics
 constexpr int kWGRows = 256;               // query rows (token, head) per workgroup
-constexpr int kWaves = 8;                  // two row blocks of 4 waves
+constexpr int kWaves = 8;                  // one query head x 32 tokens each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;                    // keys per tile
 constexpr int kRowB = 256;                 // LDS bytes per K or V row (unpadded)
@@ -457,7 +457,7 @@ __device__ __forceinline__ void dma_tile(const Args& a, const KeySrc& s, uint8_t
   }
 }
 
-// Per-wave state of a 128-row query block: Q^T (B operand), O^T accumulators
+// Per-wave state of its 32 query rows: Q^T (B operand), O^T accumulators
 // and the running exp2-domain max / lane-partial sum of each lane's row.
 struct RowState {
   bf16x8_t qb[8];

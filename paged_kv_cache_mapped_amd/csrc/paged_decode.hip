@@ -18,8 +18,9 @@
 //   * loads K with non-temporal 16-byte loads, every instruction reading
 //     whole 128-byte lines: NHD K as whole token rows (like V), turned into
 //     MFMA A-operand fragments through the wave's LDS slice; preshuffled K
-//     straight into A-operand registers, each subtile taking 8 consecutive
-//     tokens from each 16-token half of the tile,
+//     straight into A-operand registers, each subtile taking one whole
+//     16-token block (bf16) or 8 consecutive tokens from each 16-token half
+//     of the tile (fp8),
 //   * computes S^T = K Q^T for its query-head group with v_mfma_f32_16x16x32_bf16
 //     (query heads are the 16 MFMA columns; grouped-query decode is a dense
 //     contraction with G rows),
